@@ -1,0 +1,301 @@
+"""Plain CPU oracle for the H2O (Heavy-Hitter Oracle) KV-cache eviction hot path.
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check in __graft_entry__ and
+the CPU-baseline leg of bench.py may import this module. The product path (the
+HIP library and its Python binding) never imports or calls it, and this module
+imports nothing from the product path.
+
+It is slow and obviously correct on purpose: float64 NumPy, one unit
+(layer, sequence, head) at a time, no blocking, no fusion.
+
+Pages cited (by title and section):
+  [blog]     The H2O summary post at ttsmallhot.github.io/posts/8adb0d1a.html.
+             §2.1.1 attention sparsity (the scaled softmax of Q K^T / sqrt(d)),
+             §2.1.2 heavy hitters (accumulated attention score of a token),
+             §2.2 method (budget split into k_local recent + k_heavy heavy
+             hitters; the running score ledger; greedy eviction of the lowest
+             score outside the recent tokens),
+             §2.3 system implementation (evicted slot is marked free and the new
+             token's K/V is written at that address; no compaction),
+             §3.1.1 baselines (Full KV cache, Local sliding window).
+  [analysis] "H2O Heavy-Hitter Oracle 分析" (liuhc.cn).
+             §3.1 heavy-hitter identification (per head, cumulative attention
+             over the token axis, then the top-k of it),
+             §3.2 core eviction logic (score of a token = sum of its attention
+             over all steps; victim = argmin of the score; the new token always
+             joins the cache).
+
+Readings taken where the pages are silent or disagree (each is listed with its
+justification in the design notes of the repository):
+  R1  Logits are scaled by 1/sqrt(d) ([blog] §2.1.1 says the paper drops the
+      factor only for brevity).
+  R2  The recent window protects positions (t - k_local, t], the new token
+      included; eviction candidates are cached tokens with pos <= t - k_local.
+      [blog] §2.2 protects the recent tokens; [analysis] §3.2 (no window) is not
+      followed except for "the new token always joins".
+  R3  Within a decode step the new token's probabilities are added first, then
+      the victim is chosen on the updated scores; the new token's own score is
+      its own probability.
+  R4  While fewer than k slots are valid the new token is appended to the next
+      free slot and nothing is evicted; free slots take no part in attention.
+  R5  The prefill output is full causal attention over the prompt; eviction only
+      decides which K/V rows persist.
+  R6  Prefill column sums run over every causal row of the prompt.
+  R7  At prefill, heavy hitters are chosen only outside the last k_local
+      positions, ranked by (score desc, position desc): on equal score the
+      older token is dropped, matching the decode tie rule.
+  R8  After prefill the kept positions fill slots 0.. in ascending position order.
+  R9  Decode ties on score evict the oldest position.
+  R10 Scores live in fp32: prefill seeds each slot with fl32(c_j); each decode
+      step adds fl32(p) with one fp32 add. Decisions are taken on these fp32
+      values. A float64 shadow of every score is kept for the invariants.
+  R11 Eviction is per head and per layer (the analysis page's §4 notes that each
+      layer decides independently).
+  R12 k_local >= 1, so the new token is never a candidate.
+
+Near-tie adoption (the tolerance rule): when an accelerator implementation made
+a different choice whose score lies within `rel_tol` (relative) of the oracle's
+own choice, the oracle may adopt that choice so that the two states stay
+comparable; each adoption is logged on the unit. Any other disagreement raises
+ParityError.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+FREE = -1
+
+
+class ParityError(AssertionError):
+    """The other implementation's discrete choice is not a near tie."""
+
+
+# ---------------------------------------------------------------------------
+# Attention over the prompt ([blog] §2.1.1; R1, R5, R6)
+# ---------------------------------------------------------------------------
+
+def causal_softmax(Q: np.ndarray, K: np.ndarray) -> np.ndarray:
+    """P = row-softmax(Q K^T / sqrt(d)) with P_ij = 0 for j > i, in float64."""
+    T, d = Q.shape
+    S = (Q @ K.T) / math.sqrt(d)
+    future = np.triu(np.ones((T, T), dtype=bool), k=1)
+    S = np.where(future, -np.inf, S)
+    E = np.exp(S - S.max(axis=1, keepdims=True))
+    return E / E.sum(axis=1, keepdims=True)
+
+
+def column_sums(P: np.ndarray) -> np.ndarray:
+    """c_j = sum over rows i of P_ij; the causal mask makes this sum over i >= j.
+
+    This is the cumulative attention each prompt token received
+    ([analysis] §3.1: accumulate the attention scores of each token, per head).
+    """
+    return P.sum(axis=0)
+
+
+def seed_positions(c32: np.ndarray, k_heavy: int, k_local: int) -> list[int]:
+    """Positions kept after a prompt of length T = len(c32).
+
+    If T <= k every position is kept. Otherwise the last k_local positions are
+    kept ([blog] §2.2 recent tokens) plus the k_heavy highest-scoring of the
+    remaining ones ([analysis] §3.1 top-k of cumulative attention), ranked by
+    (score desc, position desc) on the fp32 scores (R7, R10).
+    """
+    T = len(c32)
+    k = k_heavy + k_local
+    if T <= k:
+        return list(range(T))
+    candidates = range(0, T - k_local)
+    ranked = sorted(candidates, key=lambda j: (-float(c32[j]), -j))
+    heavy = ranked[:k_heavy]
+    return sorted(heavy + list(range(T - k_local, T)))
+
+
+# ---------------------------------------------------------------------------
+# One unit's cache state ([blog] §2.2 budget of k slots; §2.3 slots overwritten
+# in place)
+# ---------------------------------------------------------------------------
+
+@dataclass
+class UnitCache:
+    k_heavy: int
+    k_local: int
+    head_dim: int
+    pos: np.ndarray = field(init=False)      # [k] int64, FREE = -1
+    K: np.ndarray = field(init=False)        # [k, d] float64 (exact stored values)
+    V: np.ndarray = field(init=False)
+    acc: np.ndarray = field(init=False)      # [k] float32 accumulated score
+    hist32: dict = field(init=False)         # position -> fp32 score (frozen on eviction)
+    hist64: dict = field(init=False)         # position -> float64 shadow score
+    evictions: list = field(init=False)      # (t, slot, position, fp32 score)
+    ties: list = field(init=False)           # near-tie adoptions
+    rows: int = field(init=False)            # attention rows accumulated so far
+
+    def __post_init__(self):
+        if self.k_local < 1 or self.k_heavy < 0:
+            raise ValueError("need k_local >= 1 and k_heavy >= 0 (R12)")
+        k = self.k
+        self.pos = np.full(k, FREE, dtype=np.int64)
+        self.K = np.zeros((k, self.head_dim))
+        self.V = np.zeros((k, self.head_dim))
+        self.acc = np.zeros(k, dtype=np.float32)
+        self.hist32, self.hist64 = {}, {}
+        self.evictions, self.ties = [], []
+        self.rows = 0
+
+    @property
+    def k(self) -> int:
+        return self.k_heavy + self.k_local
+
+    @property
+    def n_valid(self) -> int:
+        return int((self.pos != FREE).sum())
+
+    def kept_positions(self) -> list[int]:
+        return sorted(int(p) for p in self.pos if p != FREE)
+
+
+def _near(a: float, b: float, rel_tol: float) -> bool:
+    return abs(a - b) <= rel_tol * max(abs(a), abs(b))
+
+
+def prefill(cache: UnitCache, Q, K, V, adopt_kept=None, rel_tol=1e-5):
+    """Run the prompt through one unit and seed its cache.
+
+    Returns (O, c64): O = P V (float64, [T, d]) and the float64 column sums.
+    `adopt_kept`, if given, is another implementation's kept position set; it
+    is adopted when every position it keeps instead of the oracle's is a near
+    tie (rel_tol on the fp32 scores) with one the oracle keeps instead of it.
+    """
+    Q, K, V = (np.asarray(x, dtype=np.float64) for x in (Q, K, V))
+    T = Q.shape[0]
+    if T == 0:
+        return np.zeros((0, cache.head_dim)), np.zeros(0)
+    P = causal_softmax(Q, K)
+    O = P @ V
+    c64 = column_sums(P)
+    c32 = c64.astype(np.float32)
+    kept = seed_positions(c32, cache.k_heavy, cache.k_local)
+
+    if adopt_kept is not None:
+        other = sorted(int(p) for p in adopt_kept)
+        if other != kept:
+            theirs = set(other) - set(kept)
+            ours = set(kept) - set(other)
+            local = set(range(max(0, T - cache.k_local), T))
+            ok = (len(other) == len(kept) and not (local - set(other))
+                  and all(0 <= p < T for p in other)
+                  and all(_near(float(c32[x]), float(c32[y]), rel_tol)
+                          for x in theirs for y in ours))
+            if not ok:
+                raise ParityError(f"prefill kept sets differ beyond a near tie: "
+                                  f"only theirs {sorted(theirs)}, only ours {sorted(ours)}")
+            cache.ties.append(("prefill", T, sorted(theirs), sorted(ours)))
+            kept = other
+
+    for j in range(T):
+        cache.hist32[j] = c32[j]
+        cache.hist64[j] = float(c64[j])
+    for s, p in enumerate(kept):
+        cache.pos[s] = p
+        cache.K[s] = K[p]
+        cache.V[s] = V[p]
+        cache.acc[s] = c32[p]
+    dropped = sorted(set(range(T)) - set(kept))
+    for p in dropped:
+        cache.evictions.append((T - 1, FREE, p, c32[p]))
+    cache.rows += T
+    return O, c64
+
+
+def decode(cache: UnitCache, t: int, q, k_new, v_new, adopt_victim=None,
+           rel_tol=1e-5):
+    """One decode step for the token at position t (t = tokens seen before it).
+
+    Attention runs over the valid slots plus the new token ([blog] §2.1.1 scaled
+    softmax); each probability is added to its token's running score ([blog]
+    §2.2 score ledger; [analysis] §3.2 score = sum over steps; R3, R10). If the
+    cache is full, the candidate with the lowest (score, position) outside the
+    recent window is evicted ([blog] §2.2 greedy step; [analysis] §3.2 argmin;
+    R2, R9) and the new token's K/V overwrites that slot ([blog] §2.3). If it
+    is not full, the new token takes the next free slot (R4).
+
+    Returns (out, victim_slot): out is float64 [d]; victim_slot is the evicted
+    slot or -1 when the token was appended.
+    """
+    q, k_new, v_new = (np.asarray(x, dtype=np.float64) for x in (q, k_new, v_new))
+    n = cache.n_valid
+    assert np.all(cache.pos[:n] != FREE) and np.all(cache.pos[n:] == FREE), \
+        "valid slots must be a prefix"
+    if n > 0:
+        assert int(cache.pos[:n].max()) < t, "decode positions must increase"
+    keys = np.vstack([cache.K[:n], k_new[None, :]])
+    vals = np.vstack([cache.V[:n], v_new[None, :]])
+    s = (keys @ q) / math.sqrt(cache.head_dim)
+    e = np.exp(s - s.max())
+    p = e / e.sum()
+    out = p @ vals
+
+    p32 = p.astype(np.float32)
+    for slot in range(n):
+        cache.acc[slot] = np.float32(cache.acc[slot] + p32[slot])
+        pos = int(cache.pos[slot])
+        cache.hist32[pos] = cache.acc[slot]
+        cache.hist64[pos] += float(p[slot])
+    acc_new = p32[n]
+    cache.hist32[t] = acc_new
+    cache.hist64[t] = float(p[n])
+    cache.rows += 1
+
+    if n < cache.k:
+        slot, victim = n, -1
+    else:
+        limit = t - cache.k_local
+        cand = [s_ for s_ in range(cache.k) if cache.pos[s_] <= limit]
+        victim = min(cand, key=lambda s_: (float(cache.acc[s_]), int(cache.pos[s_])))
+        if adopt_victim is not None and int(adopt_victim) != victim:
+            g = int(adopt_victim)
+            if g not in cand or not _near(float(cache.acc[g]), float(cache.acc[victim]),
+                                          rel_tol):
+                raise ParityError(
+                    f"t={t}: victim slot {g} (pos {int(cache.pos[g]) if 0 <= g < cache.k else None}) "
+                    f"is not a near tie with the oracle's slot {victim} "
+                    f"(pos {int(cache.pos[victim])}, score {float(cache.acc[victim])!r})")
+            cache.ties.append(("decode", t, int(cache.pos[g]), int(cache.pos[victim]),
+                               float(cache.acc[g]), float(cache.acc[victim])))
+            victim = g
+        slot = victim
+        cache.evictions.append((t, slot, int(cache.pos[slot]), cache.acc[slot]))
+
+    cache.pos[slot] = t
+    cache.K[slot] = k_new
+    cache.V[slot] = v_new
+    cache.acc[slot] = acc_new
+    return out, victim
+
+
+# ---------------------------------------------------------------------------
+# Convenience: a whole unit, prompt then every decode step
+# ---------------------------------------------------------------------------
+
+def run_unit(k_heavy, k_local, Qp, Kp, Vp, qd, kd, vd, t0=None,
+             adopt_kept=None, adopt_victims=None, rel_tol=1e-5):
+    """Prefill with Qp/Kp/Vp ([T, d]) then decode rows of qd/kd/vd ([n, d]).
+
+    Returns (cache, O_prefill, c64, outs [n, d], victims [n]).
+    """
+    d = np.asarray(Qp).shape[-1] if np.asarray(Qp).size else np.asarray(qd).shape[-1]
+    cache = UnitCache(k_heavy, k_local, d)
+    O, c64 = prefill(cache, Qp, Kp, Vp, adopt_kept=adopt_kept, rel_tol=rel_tol)
+    T = np.asarray(Qp).shape[0] if t0 is None else t0
+    n = np.asarray(qd).shape[0]
+    outs = np.zeros((n, d))
+    victims = np.zeros(n, dtype=np.int64)
+    for i in range(n):
+        adopt = None if adopt_victims is None else int(adopt_victims[i])
+        outs[i], victims[i] = decode(cache, T + i, qd[i], kd[i], vd[i],
+                                     adopt_victim=adopt, rel_tol=rel_tol)
+    return cache, O, c64, outs, victims

@@ -1,0 +1,326 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of these checks retypes the oracle's formulas: they use a library routine
+(float64 scaled_dot_product_attention), closed forms (harmonic numbers, uniform
+means, exact fractions), invariants of the method (the Full and Local baselines
+of the H2O blog §3.1.1; conservation of attention mass) and an independent
+brute-force replay.
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import given, settings, strategies as st
+
+from oracle import UnitCache, ParityError, decode, prefill, run_unit, seed_positions
+from tests.bruteforce import replay
+
+
+def rand(rng, *shape, scale=1.0):
+    return rng.standard_normal(shape) * scale
+
+
+def sdpa64(Q, K, V):
+    """Full causal attention via torch's own routine, float64 on the CPU."""
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(x))[None, None] for x in (Q, K, V))
+    return torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True)[0, 0].numpy()
+
+
+def harmonic(n):
+    return sum((Fraction(1, i) for i in range(1, n + 1)), Fraction(0))
+
+
+# ---------------------------------------------------------------- prefill -------
+
+@pytest.mark.parametrize("T,d", [(1, 4), (37, 16), (128, 64)])
+def test_prefill_output_matches_library_sdpa(T, d):
+    rng = np.random.default_rng(T * 7 + d)
+    Q, K, V = rand(rng, T, d, scale=1.5), rand(rng, T, d, scale=1.5), rand(rng, T, d)
+    O, _ = prefill(UnitCache(4, 4, d), Q, K, V)
+    np.testing.assert_allclose(O, sdpa64(Q, K, V), rtol=0, atol=1e-12)
+
+
+def test_prefill_constant_values_give_constant_output():
+    rng = np.random.default_rng(3)
+    T, d = 40, 8
+    Q, K = rand(rng, T, d, scale=3), rand(rng, T, d, scale=3)
+    row = rand(rng, d)
+    O, _ = prefill(UnitCache(2, 3, d), Q, K, np.tile(row, (T, 1)))
+    np.testing.assert_allclose(O, np.tile(row, (T, 1)), rtol=0, atol=1e-12)
+
+
+def test_prefill_zero_query_column_sums_are_harmonic_tails():
+    # Q = 0 makes every causal row uniform: row i gives 1/(i+1) to each j <= i,
+    # so c_j = sum_{i=j}^{T-1} 1/(i+1) = H_T - H_j.
+    T, d = 50, 4
+    rng = np.random.default_rng(5)
+    _, c = prefill(UnitCache(5, 5, d), np.zeros((T, d)), rand(rng, T, d), rand(rng, T, d))
+    HT = harmonic(T)
+    expect = [float(HT - harmonic(j)) for j in range(T)]
+    np.testing.assert_allclose(c, expect, rtol=1e-13, atol=0)
+    assert abs(c.sum() - T) < 1e-11          # every row carries mass one
+
+
+def test_prefill_zero_query_output_is_prefix_mean():
+    T, d = 30, 6
+    rng = np.random.default_rng(8)
+    V = rand(rng, T, d)
+    O, _ = prefill(UnitCache(3, 3, d), np.zeros((T, d)), rand(rng, T, d), V)
+    expect = np.cumsum(V, axis=0) / np.arange(1, T + 1)[:, None]
+    np.testing.assert_allclose(O, expect, rtol=0, atol=1e-13)
+
+
+def test_seed_zero_query_keeps_first_heavy_and_last_local():
+    T, d, kh, kl = 50, 4, 5, 7
+    rng = np.random.default_rng(9)
+    K = rand(rng, T, d)
+    cache = UnitCache(kh, kl, d)
+    _, c = prefill(cache, np.zeros((T, d)), K, rand(rng, T, d))
+    kept = list(range(kh)) + list(range(T - kl, T))
+    assert cache.pos.tolist() == kept                       # ascending slots
+    np.testing.assert_array_equal(cache.K, K[kept])
+    HT = harmonic(T)
+    np.testing.assert_array_equal(
+        cache.acc, np.array([float(HT - harmonic(j)) for j in kept], dtype=np.float32))
+
+
+def test_seed_keeps_everything_when_prompt_fits():
+    rng = np.random.default_rng(10)
+    T, d = 6, 4
+    cache = UnitCache(4, 4, d)
+    _, c = prefill(cache, rand(rng, T, d), rand(rng, T, d), rand(rng, T, d))
+    assert cache.pos.tolist() == [0, 1, 2, 3, 4, 5, -1, -1]
+    np.testing.assert_array_equal(cache.acc[:T], c.astype(np.float32))
+    assert np.all(cache.acc[T:] == 0)
+
+
+def _seed_by_repeated_removal(c32, kh, kl):
+    T = len(c32)
+    keep = set(range(T))
+    while len(keep) > kh + kl:
+        cand = [p for p in keep if p < T - kl]
+        keep.remove(min(cand, key=lambda p: (float(c32[p]), p)))
+    return sorted(keep)
+
+
+@settings(max_examples=200, deadline=None)
+@given(st.lists(st.integers(0, 5), min_size=0, max_size=14), st.integers(0, 4), st.integers(1, 4))
+def test_seed_matches_repeated_removal_including_ties(levels, kh, kl):
+    # Few distinct levels force many exact ties; both routes must agree.
+    c32 = np.array(levels, dtype=np.float32) / 4
+    assert seed_positions(c32, kh, kl) == _seed_by_repeated_removal(c32, kh, kl)
+
+
+def test_seed_tie_drops_the_oldest():
+    c32 = np.array([1.0, 2.0, 1.0, 1.0, 0.5, 0.1], dtype=np.float32)
+    # T=6, k_local=1 keeps position 5; k_heavy=2 among 0..4: 1 (2.0) then the
+    # newest of the three tied at 1.0, which is position 3.
+    assert seed_positions(c32, 2, 1) == [1, 3, 5]
+
+
+# ---------------------------------------------------------------- decode --------
+
+def sequence(rng, N, d, scale=1.0):
+    return rand(rng, N, d, scale=scale), rand(rng, N, d, scale=scale), rand(rng, N, d)
+
+
+def run_sequence(Q, K, V, T, kh, kl):
+    return run_unit(kh, kl, Q[:T], K[:T], V[:T], Q[T:], K[T:], V[T:])
+
+
+@pytest.mark.parametrize("T,n", [(0, 20), (9, 15), (24, 8)])
+def test_full_cache_is_full_attention(T, n):
+    # Blog §3.1.1 "Full" baseline: with k >= T + n nothing is ever evicted, so every
+    # decode output is the causal attention row of the whole sequence and every
+    # score is the column sum of the whole causal softmax matrix.
+    rng = np.random.default_rng(100 + T)
+    d, N = 8, T + n
+    Q, K, V = sequence(rng, N, d, scale=1.3)
+    cache, _, _, outs, victims = run_sequence(Q, K, V, T, kh=N, kl=3)
+    full = sdpa64(Q, K, V)
+    np.testing.assert_allclose(outs, full[T:], rtol=0, atol=1e-12)
+    assert np.all(victims == -1)
+    q, k = torch.from_numpy(Q), torch.from_numpy(K)
+    S = (q @ k.T) / math.sqrt(d)
+    S = S.masked_fill(torch.triu(torch.ones(N, N, dtype=torch.bool), 1), float("-inf"))
+    colsums = torch.softmax(S, dim=1).sum(0).numpy()
+    assert cache.pos[:N].tolist() == list(range(N))
+    np.testing.assert_allclose([cache.hist64[p] for p in range(N)], colsums, rtol=1e-12)
+    np.testing.assert_allclose(cache.acc[:N], colsums, rtol=2e-6)
+
+
+@pytest.mark.parametrize("T,kl", [(0, 5), (3, 5), (30, 5), (30, 1)])
+def test_zero_heavy_budget_is_sliding_window(T, kl):
+    # Blog §3.1.1 "Local" baseline: with k_heavy = 0 the token at t attends exactly
+    # to positions max(0, t - kl) .. t, and the cache holds the last kl positions.
+    rng = np.random.default_rng(200 + T + kl)
+    d, n = 8, 25
+    N = T + n
+    Q, K, V = sequence(rng, N, d, scale=1.3)
+    cache, _, _, outs, _ = run_sequence(Q, K, V, T, kh=0, kl=kl)
+    for i, t in enumerate(range(T, N)):
+        lo = max(0, t - kl)
+        s = K[lo:t + 1] @ Q[t] / math.sqrt(d)
+        p = np.exp(s - s.max())
+        p /= p.sum()
+        np.testing.assert_allclose(outs[i], p @ V[lo:t + 1], rtol=0, atol=1e-12)
+    assert cache.kept_positions() == list(range(N - kl, N))
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_attention_mass_is_conserved(seed):
+    # Every attention row sums to one, and evicted tokens keep the score they had,
+    # so the scores of all tokens ever seen add up to the number of rows.
+    rng = np.random.default_rng(300 + seed)
+    d, T, n, kh, kl = 16, 40, 60, 6, 5
+    Q, K, V = sequence(rng, T + n, d, scale=2.0)
+    cache, _, _, _, _ = run_sequence(Q, K, V, T, kh, kl)
+    assert len(cache.hist64) == T + n and cache.rows == T + n
+    assert abs(sum(cache.hist64.values()) - (T + n)) <= 1e-9 * (T + n)
+    assert abs(sum(float(x) for x in cache.hist32.values()) - (T + n)) <= 1e-5 * (T + n)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_greedy_state_invariants_every_step(seed):
+    rng = np.random.default_rng(400 + seed)
+    d, T, n, kh, kl = 8, 12, 50, 4, 3
+    Q, K, V = sequence(rng, T + n, d, scale=2.0)
+    cache = UnitCache(kh, kl, d)
+    prefill(cache, Q[:T], K[:T], V[:T])
+    present = {p: T - p for p in range(T)}          # rows each token was present for
+    for t in range(T, T + n):
+        before = {int(p): float(a) for p, a in zip(cache.pos, cache.acc) if p >= 0}
+        _, victim = decode(cache, t, Q[t], K[t], V[t])
+        after = {int(p): float(a) for p, a in zip(cache.pos, cache.acc) if p >= 0}
+        assert len(after) == min(cache.k, t + 1)
+        assert set(range(max(0, t - kl + 1), t + 1)) <= set(after)     # window kept
+        for p in before:
+            present[p] = present.get(p, 0) + 1
+        present[t] = 1
+        if victim >= 0:
+            gone = set(before) - set(after)
+            assert len(gone) == 1
+            g = gone.pop()
+            assert g <= t - kl
+            score_g = cache.hist32[g]
+            for p, a in after.items():
+                if p <= t - kl:
+                    assert (float(score_g), g) < (a, p)                # greedy minimum
+        for p, a in after.items():
+            if p in before:
+                assert a >= before[p]                                  # never decreases
+            assert a <= present[p] + 1e-6                              # <= rows present
+
+
+def test_zero_query_decode_closed_form():
+    # Q = 0 everywhere: prompt scores are harmonic tails, every decode row is uniform
+    # over the k + 1 keys, so the kept set is {0..kh-1} plus the window at every
+    # step, the output is the mean of V over the keys, and each score is a rational
+    # closed form.
+    T, n, kh, kl, d = 20, 15, 3, 4, 5
+    k = kh + kl
+    rng = np.random.default_rng(11)
+    K = rand(rng, T + n, d)
+    V = rand(rng, T + n, d)
+    Z = np.zeros((T + n, d))
+    cache = UnitCache(kh, kl, d)
+    prefill(cache, Z[:T], K[:T], V[:T])
+    HT = harmonic(T)
+    exact = {j: HT - harmonic(j) for j in range(T)}
+    for t in range(T, T + n):
+        keys = sorted(int(p) for p in cache.pos) + [t]
+        out, _ = decode(cache, t, Z[t], K[t], V[t])
+        np.testing.assert_allclose(out, V[keys].mean(axis=0), rtol=0, atol=1e-13)
+        for p in keys[:-1]:
+            exact[p] += Fraction(1, k + 1)
+        exact[t] = Fraction(1, k + 1)
+        assert cache.kept_positions() == list(range(kh)) + list(range(t - kl + 1, t + 1))
+    for p in cache.kept_positions():
+        assert abs(cache.hist64[p] - float(exact[p])) < 1e-13
+        assert abs(float(cache.hist32[p]) - float(exact[p])) <= 1e-6 * float(exact[p])
+
+
+def test_decode_tie_evicts_the_oldest():
+    d = 4
+    cache = UnitCache(2, 2, d)
+    cache.pos[:] = [3, 1, 5, 6]
+    cache.acc[:] = 1.0
+    cache.K[:] = 0.25
+    for p in (3, 1, 5, 6):
+        cache.hist32[p], cache.hist64[p] = np.float32(1.0), 1.0
+    _, victim = decode(cache, 7, np.ones(d), np.full(d, 0.25), np.ones(d))
+    # Candidates are positions <= 7 - 2 = 5, i.e. {3, 1, 5}, all tied: oldest (1) goes.
+    assert victim == 1 and cache.pos.tolist() == [3, 7, 5, 6]
+
+
+def test_near_tie_adoption_accepts_ties_and_rejects_the_rest():
+    d = 4
+    def fresh():
+        c = UnitCache(2, 2, d)
+        c.pos[:] = [3, 1, 5, 6]
+        c.acc[:] = [1.0, 1.0000001, 2.0, 3.0]
+        c.K[:] = 0.25
+        for p, a in zip(c.pos, c.acc):
+            c.hist32[int(p)], c.hist64[int(p)] = a, float(a)
+        return c
+    c = fresh()
+    _, v = decode(c, 7, np.ones(d), np.full(d, 0.25), np.ones(d), adopt_victim=1)
+    assert v == 1 and len(c.ties) == 1
+    with pytest.raises(ParityError):
+        decode(fresh(), 7, np.ones(d), np.full(d, 0.25), np.ones(d), adopt_victim=2)
+    with pytest.raises(ParityError):   # position 6 is inside the window
+        decode(fresh(), 7, np.ones(d), np.full(d, 0.25), np.ones(d), adopt_victim=3)
+
+
+# ------------------------------------------------------------ brute force -------
+
+def _oracle_victim_positions(cache):
+    return [(t, p) for (t, slot, p, _) in cache.evictions if slot != -1]
+
+
+@settings(max_examples=120, deadline=None)
+@given(T=st.integers(0, 8), n=st.integers(0, 12), kh=st.integers(0, 3), kl=st.integers(1, 3),
+       d=st.integers(1, 4), seed=st.integers(0, 10_000))
+def test_brute_force_replay_random(T, n, kh, kl, d, seed):
+    rng = np.random.default_rng(seed)
+    N = T + n
+    Q, K, V = sequence(rng, N, d, scale=1.5)
+    bf = replay(Q.tolist(), K.tolist(), V.tolist(), T, kh, kl)
+    if any(g < 1e-5 for g in bf["gaps"]):
+        return                         # near tie: either choice is valid
+    c32 = None
+    cache, _, c64, outs, _ = run_sequence(Q, K, V, T, kh, kl)
+    if T > 0:
+        c32 = c64.astype(np.float32)
+        srt = sorted(c32[: max(0, T - kl)])
+        if any(abs(a - b) <= 1e-5 * max(a, b) for a, b in zip(srt, srt[1:])):
+            return
+    assert [int(p) for p in sorted(cache.pos) if p >= 0] == bf["kept"]
+    assert _oracle_victim_positions(cache) == bf["victims"]
+    if n:
+        np.testing.assert_allclose(outs, np.array(bf["outs"]), rtol=0, atol=1e-12)
+    for p in range(N):
+        assert abs(cache.hist64[p] - bf["scores"][p]) <= 1e-12 * max(1.0, bf["scores"][p])
+
+
+@pytest.mark.parametrize("T,n,kh,kl", [(0, 12, 2, 2), (5, 10, 1, 2), (8, 12, 3, 3), (6, 9, 0, 2)])
+def test_brute_force_replay_exact_uniform(T, n, kh, kl):
+    # Q = 0: every row uniform; the replay runs in exact fractions, so exact ties
+    # between equal scores do occur and must resolve the same way.
+    d = 3
+    rng = np.random.default_rng(T * 100 + n)
+    N = T + n
+    K, V = rand(rng, N, d), rand(rng, N, d)
+    Z = np.zeros((N, d))
+    bf = replay([[0.0] * d] * N, K.tolist(), V.tolist(), T, kh, kl, uniform=True)
+    cache, _, c64, outs, _ = run_sequence(Z, K, V, T, kh, kl)
+    assert [int(p) for p in sorted(cache.pos) if p >= 0] == bf["kept"]
+    assert _oracle_victim_positions(cache) == bf["victims"]
+    np.testing.assert_allclose(outs, np.array([[float(x) for x in o] for o in bf["outs"]]),
+                               rtol=0, atol=1e-12)
+    for p in range(N):
+        assert abs(cache.hist64[p] - float(bf["scores"][p])) < 1e-12
