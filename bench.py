@@ -1,0 +1,243 @@
+"""Throughput of the H2O hot path on one MI355X, as one JSON line.
+
+Workload: the OPT-6.7B-shaped layer — batch 8, 32 heads, head_dim 128, fp16
+K/V, a 512-token padded prompt plus 32 generated tokens, k = 52 heavy + 52
+local slots (20% of the prompt). Inputs are seeded synthetic draws, generated
+on the device before timing.
+
+One step = one pass of the whole hot path over the batch: reset, prefill
+(causal attention + column sums + cache seeding) and 32 decode steps (fused
+attention + score accumulation + masked argmin + in-place overwrite). `value`
+is generated tokens per second of the whole step (batch * 32 / step time), the
+end-to-end token throughput the H2O blog's §3.1.3 defines; the decode-phase
+and prefill-phase rates are reported beside it.
+
+Timing:
+  * timed loop: each step replays two HIP graphs (reset+prefill, then the 32
+    decode launches) with HIP events around each phase, on torch's stream;
+  * kernel pass: the same steps launched eagerly with a HIP event pair around
+    every h2o_decode_step / h2o_prefill call, which gives each launch's device
+    duration for the roofline figures;
+  * cpu_baseline: the CPU oracle on the same inputs (all 256 units of one step).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published
+METRIC = "H2O decode tokens/s at 20% KV budget + % of HBM roofline (prefill % MFMA peak)"
+
+
+def decode_bytes_per_unit(w) -> int:
+    """Algorithmic HBM bytes of one decode step of one unit."""
+    k, d, s = w.k, w.head_dim, w.elem_bytes
+    return 2 * k * d * s + 12 * k + 3 * d * s + 4 * d + 2 * d * s + 8
+
+
+def prefill_flops_per_unit(w) -> int:
+    """Causal QK^T and PV, diagonal included: 2 * T(T+1)/2 * 2d."""
+    T, d = w.prompt, w.head_dim
+    return 2 * T * (T + 1) * d
+
+
+def prefill_bytes_per_unit(w) -> int:
+    T, d, s, k = w.prompt, w.head_dim, w.elem_bytes, w.k
+    return 3 * T * d * s + 4 * T * d + 4 * T + 2 * k * d * s + 8 * k
+
+
+def cpu_baseline(w, x, units):
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import run_unit
+    host = {k: v.double().cpu().numpy() for k, v in x.items()}
+    t0 = time.perf_counter()
+    for uidx in units:
+        b, h = divmod(uidx, w.heads)
+        run_unit(w.k_heavy, w.k_local, host["q_prompt"][b, h], host["k_prompt"][b, h],
+                 host["v_prompt"][b, h], host["q_dec"][:, b, h], host["k_dec"][:, b, h],
+                 host["v_dec"][:, b, h])
+    dt = time.perf_counter() - t0
+    per_unit = dt / len(units)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    tokens_per_s = w.batch * w.steps / (per_unit * w.units_per_layer)
+    del np
+    return {"value": tokens_per_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(units)} of {w.units_per_layer} units (prefill + {w.steps} decode "
+                      f"steps each) in {dt:.1f} s, scaled to the whole step"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the H2O path has no cross-GPU exchange and this "
+              "build runs on a single MI355X; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from kv_cache_eviction_03_amd import H2OCache
+    from workloads import WORKLOADS, generate
+
+    w = WORKLOADS[2]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x = generate(w, seed=args.seed, device=dev)
+    B, H, d, T, n = w.batch, w.heads, w.head_dim, w.prompt, w.steps
+    units = w.units_per_layer
+
+    cache = H2OCache(B, H, d, w.k_heavy, w.k_local, w.torch_dtype, dev, max_prompt=T)
+    out_p = torch.empty((B, H, T, d), dtype=torch.float32, device=dev)
+    colsum = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    outs = torch.empty((n, B, H, d), dtype=torch.float32, device=dev)
+
+    def run_prefill():
+        cache.reset()
+        cache.prefill(x["q_prompt"], x["k_prompt"], x["v_prompt"], out=out_p, colsum=colsum)
+
+    def run_decode():
+        for i in range(n):
+            cache.decode(x["q_dec"][i], x["k_dec"][i], x["v_dec"][i], out=outs[i])
+
+    # Eager reference run (also warms up the kernels).
+    run_prefill()
+    run_decode()
+    torch.cuda.synchronize()
+    ref_state = {k: v.clone() for k, v in cache.state().items() if torch.is_tensor(v)}
+    ref_outs = outs.clone()
+
+    # Capture the two phases as HIP graphs.
+    side = torch.cuda.Stream(dev)
+    g_pre, g_dec = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g_pre, stream=side):
+            run_prefill()
+        cache.t = T
+        with torch.cuda.graph(g_dec, stream=side):
+            run_decode()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        g_pre.replay()
+        g_dec.replay()
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for e0, e1, e2 in ev:
+        e0.record(stream)
+        g_pre.replay()
+        e1.record(stream)
+        g_dec.replay()
+        e2.record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(end)
+    pre_ms = sum(a.elapsed_time(b) for a, b, _ in ev) / args.steps
+    dec_ms = sum(b.elapsed_time(c) for _, b, c in ev) / args.steps
+    ms_per_step = total_ms / args.steps
+
+    # Graph replays must reproduce the eager run bit for bit.
+    for k, v in ref_state.items():
+        if not torch.equal(getattr(cache, k), v):
+            raise RuntimeError(f"graph replay diverged from the eager run in {k}")
+    if not torch.equal(outs, ref_outs):
+        raise RuntimeError("graph replay diverged from the eager run in decode outputs")
+
+    # Kernel pass: eager launches with an event pair around every call.
+    kp = max(3, min(args.steps, 10))
+    dec_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(kp * n)]
+    pre_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(kp)]
+    for s_ in range(kp):
+        cache.reset()
+        a, b = pre_ev[s_]
+        a.record(stream)
+        cache.prefill(x["q_prompt"], x["k_prompt"], x["v_prompt"], out=out_p, colsum=colsum)
+        b.record(stream)
+        for i in range(n):
+            a, b = dec_ev[s_ * n + i]
+            a.record(stream)
+            cache.decode(x["q_dec"][i], x["k_dec"][i], x["v_dec"][i], out=outs[i])
+            b.record(stream)
+    torch.cuda.synchronize()
+    dec_kernel_us = 1e3 * sum(a.elapsed_time(b) for a, b in dec_ev) / len(dec_ev)
+    pre_call_us = 1e3 * sum(a.elapsed_time(b) for a, b in pre_ev) / len(pre_ev)
+
+    dec_bytes = decode_bytes_per_unit(w) * units
+    dec_gbs = dec_bytes / (dec_kernel_us * 1e-6) / 1e9
+    pre_flops = prefill_flops_per_unit(w) * units
+    pre_tflops = pre_flops / (pre_call_us * 1e-6) / 1e12
+    pre_gbs = prefill_bytes_per_unit(w) * units / (pre_call_us * 1e-6) / 1e9
+
+    tokens = B * n
+    value = tokens / (ms_per_step * 1e-3)
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: batch {B}, {H} heads, head_dim {d}, fp16 K/V, prompt {T} + "
+                        f"{n} generated, k = {w.k_heavy} heavy + {w.k_local} local slots",
+            "step": f"reset + prefill ({T} tokens) + {n} decode steps, replayed as HIP graphs",
+            "value_is": "generated tokens / step time (prefill + decode)",
+            "global_batch": B, "seq_len": T + n, "parallelism": "single GPU",
+        },
+        "decode_tokens_per_s": tokens / (dec_ms * 1e-3),
+        "prefill_tokens_per_s": B * T / (pre_ms * 1e-3),
+        "phase_ms": {"prefill": pre_ms, "decode": dec_ms},
+        "roofline": {
+            "bound": "hbm", "kernel": "decode_kernel<_Float16,128> (one launch per decode step)",
+            "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": dec_gbs / HBM_PEAK_GBS, "traffic": None,
+            "avg_launch_us": dec_kernel_us, "algorithmic_bytes_per_launch": dec_bytes,
+        },
+        "roofline_prefill": {
+            "bound": "hbm (arithmetic intensity %.1f flop/B < ridge 312.5)" % (
+                prefill_flops_per_unit(w) / prefill_bytes_per_unit(w)),
+            "achieved_tflops": pre_tflops, "mfma_peak_tflops": MFMA_F16_PEAK_TFLOPS,
+            "mfma_frac": pre_tflops / MFMA_F16_PEAK_TFLOPS,
+            "achieved_gbs": pre_gbs, "hbm_frac": pre_gbs / HBM_PEAK_GBS,
+            "avg_call_us": pre_call_us,
+            "note": "one h2o_prefill call = attention + column-sum + seed kernels",
+        },
+        "wall_s_timed_loop": wall,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, x, list(range(units)))
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

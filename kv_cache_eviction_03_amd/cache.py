@@ -1,0 +1,115 @@
+"""Torch-side owner of one layer's H2O cache: device buffers, the host position
+counter t, and calls into the C ABI on torch's current HIP stream.
+
+PyTorch supplies device memory and the stream only; every step of the method
+runs in the HIP kernels behind the C ABI.
+"""
+from __future__ import annotations
+
+import torch
+
+from ._abi import (H2O_BF16, H2O_F16, H2O_F32, CacheDesc, DecodeAux, check, h2o_decode_step,
+                   h2o_prefill, h2o_reset, h2o_workspace_bytes)
+
+_DTYPE_CODE = {torch.float32: H2O_F32, torch.float16: H2O_F16, torch.bfloat16: H2O_BF16}
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(x: torch.Tensor | None) -> int:
+    return 0 if x is None else x.data_ptr()
+
+
+class H2OCache:
+    """k = k_heavy + k_local slots per (sequence, head) of one layer."""
+
+    def __init__(self, batch: int, heads: int, head_dim: int, k_heavy: int, k_local: int,
+                 dtype: torch.dtype, device="cuda", max_prompt: int = 0):
+        if dtype not in _DTYPE_CODE:
+            raise ValueError(f"unsupported dtype {dtype}")
+        self.batch, self.heads, self.head_dim = batch, heads, head_dim
+        self.k_heavy, self.k_local = k_heavy, k_local
+        self.k = k_heavy + k_local
+        self.dtype = dtype
+        dev = torch.device(device)
+        if dev.type == "cuda" and dev.index is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+        self.device = dev
+        shape = (batch, heads, self.k, head_dim)
+        self.k_slots = torch.zeros(shape, dtype=dtype, device=self.device)
+        self.v_slots = torch.zeros(shape, dtype=dtype, device=self.device)
+        self.slot_pos = torch.full((batch, heads, self.k), -1, dtype=torch.int32,
+                                   device=self.device)
+        self.acc_score = torch.zeros((batch, heads, self.k), dtype=torch.float32,
+                                     device=self.device)
+        self.t = 0
+        self.workspace = torch.empty(0, dtype=torch.uint8, device=self.device)
+        self.reserve(max_prompt)
+
+    def desc(self) -> CacheDesc:
+        return CacheDesc(self.batch, self.heads, self.head_dim, self.k_heavy, self.k_local,
+                         _DTYPE_CODE[self.dtype], self.k_slots.data_ptr(),
+                         self.v_slots.data_ptr(), self.slot_pos.data_ptr(),
+                         self.acc_score.data_ptr())
+
+    def reserve(self, max_prompt: int) -> None:
+        need = h2o_workspace_bytes(self.desc(), max_prompt)
+        if need > self.workspace.numel():
+            self.workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
+
+    def _check(self, x: torch.Tensor, shape, name: str) -> None:
+        if x.dtype != self.dtype or tuple(x.shape) != tuple(shape) or not x.is_contiguous() \
+                or x.device != self.device:
+            raise ValueError(f"{name}: expected contiguous {self.dtype} {tuple(shape)} on "
+                             f"{self.device}, got {x.dtype} {tuple(x.shape)} on {x.device}")
+
+    def reset(self) -> None:
+        check(h2o_reset(self.desc(), _stream(self.device)), "h2o_reset")
+        self.t = 0
+
+    def prefill(self, q, k, v, out=None, colsum=None, want_colsum=True):
+        """q, k, v: [B, H, T, d]. Returns (out [B, H, T, d] fp32, colsum [B, H, T] or None)."""
+        T = q.shape[2]
+        shape = (self.batch, self.heads, T, self.head_dim)
+        for x, name in ((q, "q"), (k, "k"), (v, "v")):
+            self._check(x, shape, name)
+        if out is None:
+            out = torch.empty(shape, dtype=torch.float32, device=self.device)
+        if colsum is None and want_colsum:
+            colsum = torch.empty(shape[:3], dtype=torch.float32, device=self.device)
+        self.reserve(T)
+        check(h2o_prefill(self.desc(), q.data_ptr(), k.data_ptr(), v.data_ptr(), T,
+                          out.data_ptr(), _ptr(colsum), self.workspace.data_ptr(),
+                          self.workspace.numel(), _stream(self.device)), "h2o_prefill")
+        self.t = T
+        return out, colsum
+
+    def decode(self, q, k_new, v_new, out=None, victim_slot=None, evicted_pos=None,
+               evicted_acc=None):
+        """q, k_new, v_new: [B, H, d]. Returns out [B, H, d] fp32; advances t by one."""
+        shape = (self.batch, self.heads, self.head_dim)
+        for x, name in ((q, "q"), (k_new, "k_new"), (v_new, "v_new")):
+            self._check(x, shape, name)
+        if out is None:
+            out = torch.empty(shape, dtype=torch.float32, device=self.device)
+        aux = None
+        if victim_slot is not None or evicted_pos is not None or evicted_acc is not None:
+            aux = DecodeAux(_ptr(victim_slot), _ptr(evicted_pos), _ptr(evicted_acc))
+        ws = self.workspace
+        check(h2o_decode_step(self.desc(), self.t, q.data_ptr(), k_new.data_ptr(),
+                              v_new.data_ptr(), out.data_ptr(), aux, ws.data_ptr(), ws.numel(),
+                              _stream(self.device)), "h2o_decode_step")
+        self.t += 1
+        return out
+
+    def state(self) -> dict:
+        """The whole cache state (for checkpoints): tensors plus the host counter t."""
+        return {"k_slots": self.k_slots, "v_slots": self.v_slots, "slot_pos": self.slot_pos,
+                "acc_score": self.acc_score, "t": self.t}
+
+    def load_state(self, st: dict) -> None:
+        for name in ("k_slots", "v_slots", "slot_pos", "acc_score"):
+            getattr(self, name).copy_(st[name])
+        self.t = int(st["t"])

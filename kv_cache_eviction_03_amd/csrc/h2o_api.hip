@@ -1,0 +1,187 @@
+// C ABI of the H2O hot path (declared in include/h2o.h): argument checks,
+// dtype / head_dim dispatch, workspace carving and kernel enqueue.
+//
+// Every check runs on the host before the first HIP call, so a rejected call
+// enqueues nothing, touches no memory and needs no device (the checks are
+// exercised without a GPU). No call allocates, frees or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/h2o.h"
+#include "h2o_kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+h2o_status fail(h2o_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+h2o_status hip_fail(hipError_t e, const char* what) {
+  return fail(H2O_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t elem_bytes(int32_t dt) { return dt == H2O_F32 ? 4 : 2; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+constexpr size_t kWsAlign = 256;
+
+h2o_status check_desc(const h2o_cache_desc* c) {
+  if (!c) return fail(H2O_ERR_INVALID, "cache descriptor is NULL");
+  if (c->batch < 1 || c->heads < 1)
+    return fail(H2O_ERR_INVALID, "batch (%d) and heads (%d) must be >= 1", c->batch, c->heads);
+  if (c->dtype != H2O_F32 && c->dtype != H2O_F16 && c->dtype != H2O_BF16)
+    return fail(H2O_ERR_INVALID, "dtype %d is not an h2o_dtype", c->dtype);
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(H2O_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", c->head_dim);
+  if (c->k_heavy < 0) return fail(H2O_ERR_INVALID, "k_heavy %d < 0", c->k_heavy);
+  if (c->k_local < 1)
+    return fail(H2O_ERR_INVALID, "k_local %d < 1: the new token must stay in the recent window",
+                c->k_local);
+  if ((int64_t)c->k_heavy + c->k_local > H2O_MAX_SLOTS)
+    return fail(H2O_ERR_UNSUPPORTED, "k = %lld exceeds H2O_MAX_SLOTS (%d)",
+                (long long)c->k_heavy + c->k_local, H2O_MAX_SLOTS);
+  if ((int64_t)c->batch * c->heads > 0x7fffffffLL)
+    return fail(H2O_ERR_UNSUPPORTED, "batch * heads exceeds 2^31 - 1");
+  if (!c->k_slots || !c->v_slots || !c->slot_pos || !c->acc_score)
+    return fail(H2O_ERR_INVALID, "a cache array pointer is NULL");
+  if (!aligned(c->k_slots, 16) || !aligned(c->v_slots, 16))
+    return fail(H2O_ERR_INVALID, "k_slots / v_slots must be 16-byte aligned");
+  if (!aligned(c->slot_pos, 4) || !aligned(c->acc_score, 4))
+    return fail(H2O_ERR_INVALID, "slot_pos / acc_score must be 4-byte aligned");
+  return H2O_OK;
+}
+
+size_t prefill_ws(const h2o_cache_desc* c, int64_t T) {
+  const size_t rows = (size_t)c->batch * c->heads * (size_t)T;
+  return 2 * round_up(rows * sizeof(float), kWsAlign);   // log-sum-exp + column sums
+}
+
+size_t decode_ws(const h2o_cache_desc*) { return 0; }
+
+h2o::DType dtype_of(const h2o_cache_desc* c) { return static_cast<h2o::DType>(c->dtype); }
+
+float qk_scale(int d) { return (float)(1.4426950408889634 / std::sqrt((double)d)); }
+
+}  // namespace
+
+extern "C" {
+
+const char* h2o_status_str(h2o_status s) {
+  switch (s) {
+    case H2O_OK: return "H2O_OK";
+    case H2O_ERR_INVALID: return "H2O_ERR_INVALID";
+    case H2O_ERR_UNSUPPORTED: return "H2O_ERR_UNSUPPORTED";
+    case H2O_ERR_WORKSPACE: return "H2O_ERR_WORKSPACE";
+    case H2O_ERR_HIP: return "H2O_ERR_HIP";
+  }
+  return "H2O_ERR_UNKNOWN";
+}
+
+const char* h2o_last_error(void) { return g_err; }
+
+size_t h2o_workspace_bytes(const h2o_cache_desc* c, int32_t max_prompt) {
+  if (check_desc(c) != H2O_OK || max_prompt < 0) return 0;
+  const size_t a = prefill_ws(c, max_prompt), b = decode_ws(c);
+  return a > b ? a : b;
+}
+
+h2o_status h2o_reset(const h2o_cache_desc* c, void* stream) {
+  g_err[0] = 0;
+  if (h2o_status st = check_desc(c)) return st;
+  h2o::ResetParams p{c->slot_pos, c->acc_score,
+                     (int64_t)c->batch * c->heads * (c->k_heavy + c->k_local)};
+  if (hipError_t e = h2o::launch_reset(p, static_cast<hipStream_t>(stream)))
+    return hip_fail(e, "reset launch");
+  return H2O_OK;
+}
+
+h2o_status h2o_prefill(const h2o_cache_desc* c, const void* q, const void* k, const void* v,
+                       int32_t T, float* out, float* colsum_out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  if (h2o_status st = check_desc(c)) return st;
+  if (T < 0) return fail(H2O_ERR_INVALID, "prompt length T = %d < 0", T);
+  if (!q || !k || !v || !out) return fail(H2O_ERR_INVALID, "q, k, v and out must not be NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return fail(H2O_ERR_INVALID, "q, k, v and out must be 16-byte aligned");
+  if (colsum_out && !aligned(colsum_out, 4))
+    return fail(H2O_ERR_INVALID, "colsum_out must be 4-byte aligned");
+  const int64_t units = (int64_t)c->batch * c->heads;
+  if (units * (((int64_t)T + 15) / 16) > 0x7fffffffLL)
+    return fail(H2O_ERR_UNSUPPORTED, "batch * heads * ceil(T / 16) exceeds the grid limit");
+  const size_t need = prefill_ws(c, T);
+  if (T > 0 && (!workspace || workspace_bytes < need))
+    return fail(H2O_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
+                workspace ? workspace_bytes : (size_t)0, need);
+  if (workspace && !aligned(workspace, kWsAlign))
+    return fail(H2O_ERR_INVALID, "workspace must be %zu-byte aligned", kWsAlign);
+  if (T == 0) return H2O_OK;
+
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  const size_t rows_bytes = round_up((size_t)units * T * sizeof(float), kWsAlign);
+  float* lse2 = reinterpret_cast<float*>(ws);
+  float* colsum = colsum_out ? colsum_out : reinterpret_cast<float*>(ws + rows_bytes);
+  const int D = c->head_dim;
+  const h2o::DType dt = dtype_of(c);
+
+  h2o::PrefillParams pp{q, k, v, out, lse2, colsum, (int32_t)units, T, qk_scale(D)};
+  hipError_t e;
+  if (dt == h2o::DType::F32) {
+    if ((e = h2o::launch_prefill_attn_f32(D, pp, s))) return hip_fail(e, "prefill attention launch");
+    if ((e = h2o::launch_prefill_colsum_f32(D, pp, s))) return hip_fail(e, "prefill colsum launch");
+  } else {
+    if ((e = h2o::launch_prefill_attn_mfma(dt, D, pp, s)))
+      return hip_fail(e, "prefill attention launch");
+    if ((e = h2o::launch_prefill_colsum_mfma(dt, D, pp, s)))
+      return hip_fail(e, "prefill colsum launch");
+  }
+  h2o::SeedParams sp{k, v, colsum, c->k_slots, c->v_slots, c->slot_pos, c->acc_score,
+                     (int32_t)units, T, c->k_heavy, c->k_local};
+  if ((e = h2o::launch_seed(dt, D, sp, s))) return hip_fail(e, "seed launch");
+  return H2O_OK;
+}
+
+h2o_status h2o_decode_step(const h2o_cache_desc* c, int64_t t, const void* q, const void* k_new,
+                           const void* v_new, float* out, const h2o_decode_aux* aux,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  (void)workspace;
+  (void)workspace_bytes;
+  if (h2o_status st = check_desc(c)) return st;
+  if (t < 0 || t >= (int64_t)H2O_MAX_POSITION)
+    return fail(H2O_ERR_INVALID, "position t = %lld outside [0, 2^31 - 1)", (long long)t);
+  if (!q || !k_new || !v_new || !out)
+    return fail(H2O_ERR_INVALID, "q, k_new, v_new and out must not be NULL");
+  if (!aligned(q, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(out, 16))
+    return fail(H2O_ERR_INVALID, "q, k_new, v_new and out must be 16-byte aligned");
+  if (aux && ((aux->victim_slot && !aligned(aux->victim_slot, 4)) ||
+              (aux->evicted_pos && !aligned(aux->evicted_pos, 4)) ||
+              (aux->evicted_acc && !aligned(aux->evicted_acc, 4))))
+    return fail(H2O_ERR_INVALID, "aux arrays must be 4-byte aligned");
+
+  const int D = c->head_dim;
+  const int32_t kk = c->k_heavy + c->k_local;
+  h2o::DecodeParams p{q, k_new, v_new, c->k_slots, c->v_slots, c->slot_pos, c->acc_score, out,
+                      aux ? aux->victim_slot : nullptr, aux ? aux->evicted_pos : nullptr,
+                      aux ? aux->evicted_acc : nullptr, (int32_t)(c->batch * c->heads), kk,
+                      c->k_local, (int32_t)t, qk_scale(D)};
+  if (hipError_t e = h2o::launch_decode(dtype_of(c), D, p, static_cast<hipStream_t>(stream)))
+    return hip_fail(e, "decode launch");
+  return H2O_OK;
+}
+
+}  // extern "C"

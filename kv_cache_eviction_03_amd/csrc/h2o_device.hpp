@@ -1,0 +1,93 @@
+// Device-side helpers shared by the H2O kernels for gfx950: storage types,
+// 16-byte chunk loads with conversion to fp32, wave reductions, MFMA wrappers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace h2o {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kWave = 64;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// Elements of T in one 16-byte chunk.
+template <typename T> struct Chunk { static constexpr int N = 16 / sizeof(T); };
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// Unpack a 16-byte chunk of T into fp32.
+__device__ __forceinline__ void unpack(const uint4& v, float (&f)[4], float) {
+  f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+  f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+}
+__device__ __forceinline__ void unpack(const uint4& v, float (&f)[8], _Float16) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] & 0xffffu));
+    f[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] >> 16));
+  }
+}
+__device__ __forceinline__ void unpack(const uint4& v, float (&f)[8], __bf16) {
+  // bf16 -> fp32 is exact: the bf16 bits are the top half of the fp32 bits.
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void load_f32(const T* p, float (&f)[Chunk<T>::N]) {
+  unpack(ld16(p), f, T{});
+}
+
+// Butterfly reductions over groups of `width` consecutive lanes (width a power of two <= 64).
+template <int WIDTH>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int o = WIDTH / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+template <int WIDTH>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int o = WIDTH / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
+  const uint32_t lo = __shfl_xor((uint32_t)v, o, kWave);
+  const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, kWave);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint64_t w = shfl_xor_u64(v, o);
+    v = w < v ? w : v;
+  }
+  return v;
+}
+
+// 16x16x32 MFMA, fp32 accumulate (gfx950). Lane l supplies A[l%16][k-group l/16]
+// and B[k-group l/16][l%16]; D[4*(l/16)+i][l%16] comes back in element i.
+__device__ __forceinline__ f32x4 mfma16x16x32(const f16x8& a, const f16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <typename T> struct Vec8;
+template <> struct Vec8<_Float16> { typedef f16x8 type; typedef f16x4 half; };
+template <> struct Vec8<__bf16> { typedef bf16x8 type; typedef bf16x4 half; };
+
+}  // namespace h2o

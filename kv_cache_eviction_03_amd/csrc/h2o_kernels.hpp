@@ -1,0 +1,77 @@
+// Kernel parameter blocks and host-side launchers of the H2O HIP kernels.
+// The launchers assume validated arguments (the C-ABI layer checks them).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace h2o {
+
+enum class DType : int { F32 = 0, F16 = 1, BF16 = 2 };
+
+struct DecodeParams {
+  const void* q;        // [units][D]
+  const void* k_new;    // [units][D]
+  const void* v_new;    // [units][D]
+  void* k_slots;        // [units][k][D]
+  void* v_slots;        // [units][k][D]
+  int32_t* slot_pos;    // [units][k]
+  float* acc;           // [units][k]
+  float* out;           // [units][D] fp32
+  int32_t* victim_slot; // [units] or null
+  int32_t* evicted_pos; // [units] or null
+  float* evicted_acc;   // [units] or null
+  int32_t units;
+  int32_t k;
+  int32_t k_local;
+  int32_t t;
+  float qk_scale;       // log2(e) / sqrt(D): logits are kept in the log2 domain
+};
+
+struct PrefillParams {
+  const void* q;        // [units][T][D]
+  const void* k;
+  const void* v;
+  float* out;           // [units][T][D]
+  float* lse2;          // [units][T] row log-sum-exp, log2 domain (workspace)
+  float* colsum;        // [units][T]
+  int32_t units;
+  int32_t T;
+  float qk_scale;       // log2(e) / sqrt(D)
+};
+
+struct SeedParams {
+  const void* k;        // prompt K/V [units][T][D]
+  const void* v;
+  const float* colsum;  // [units][T]
+  void* k_slots;
+  void* v_slots;
+  int32_t* slot_pos;
+  float* acc;
+  int32_t units;
+  int32_t T;
+  int32_t k_heavy;
+  int32_t k_local;
+};
+
+struct ResetParams {
+  int32_t* slot_pos;
+  float* acc;
+  int64_t n;            // units * k
+};
+
+hipError_t launch_reset(const ResetParams& p, hipStream_t s);
+hipError_t launch_decode(DType dt, int D, const DecodeParams& p, hipStream_t s);
+// fp16 / bf16 storage: MFMA kernels.
+hipError_t launch_prefill_attn_mfma(DType dt, int D, const PrefillParams& p, hipStream_t s);
+hipError_t launch_prefill_colsum_mfma(DType dt, int D, const PrefillParams& p, hipStream_t s);
+// fp32 storage: vector-ALU kernels.
+hipError_t launch_prefill_attn_f32(int D, const PrefillParams& p, hipStream_t s);
+hipError_t launch_prefill_colsum_f32(int D, const PrefillParams& p, hipStream_t s);
+hipError_t launch_seed(DType dt, int D, const SeedParams& p, hipStream_t s);
+
+// Dynamic LDS bytes the decode kernel needs for k slots.
+size_t decode_lds_bytes(DType dt, int D, int k);
+
+}  // namespace h2o

@@ -1,0 +1,128 @@
+// Prefill kernels for fp32 storage (vector ALU, no MFMA).
+//
+// Same two outputs as the MFMA kernels: causal attention with each row's
+// log-sum-exp (H2O blog, ttsmallhot.github.io, §2.1.1), then the softmax
+// column sums c_j = sum_{i >= j} P_ij ("H2O Heavy-Hitter Oracle 分析", §3.1)
+// re-formed from the stored log-sum-exp in a fixed order.
+//
+// Layout: 16 rows per workgroup, 16 lanes per row, each lane owning D/16
+// consecutive dims; a logit is a 16-lane butterfly sum, so both kernels form
+// bit-identical logits for the same (query, key) pair.
+#include "h2o_device.hpp"
+#include "h2o_kernels.hpp"
+
+namespace h2o {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int RB = 16;  // rows per workgroup
+
+template <int D>
+__device__ __forceinline__ void load_part(const float* row, int part, float (&x)[D / 16]) {
+#pragma unroll
+  for (int c = 0; c < D / 64; ++c) {
+    float f[4];
+    load_f32(row + part * (D / 16) + 4 * c, f);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[4 * c + i] = f[i];
+  }
+}
+
+template <int D>
+__device__ __forceinline__ float dot16(const float (&a)[D / 16], const float (&b)[D / 16]) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) s = fmaf(a[i], b[i], s);
+  return group_sum<16>(s);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void attn_f32_kernel(PrefillParams p) {
+  constexpr int DP = D / 16;
+  const int T_ = p.T;
+  const int nqb = (T_ + RB - 1) / RB;
+  const int r = blockIdx.x / p.units;
+  const int unit = blockIdx.x - r * p.units;
+  const int qb = nqb - 1 - r;
+  const int qi = threadIdx.x / 16, part = threadIdx.x % 16;
+  const int q = qb * RB + qi;
+  const int qc = q < T_ ? q : T_ - 1;   // rows past T compute a copy, never stored
+  const size_t base = (size_t)unit * T_ * D;
+  const float* Q = static_cast<const float*>(p.q) + base;
+  const float* K = static_cast<const float*>(p.k) + base;
+  const float* V = static_cast<const float*>(p.v) + base;
+
+  float qv[DP];
+  load_part<D>(Q + (size_t)qc * D, part, qv);
+  float o[DP];
+#pragma unroll
+  for (int i = 0; i < DP; ++i) o[i] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  const int jmax = min(qb * RB + RB - 1, T_ - 1);   // uniform over the workgroup
+  for (int j = 0; j <= jmax; ++j) {
+    float kv[DP], vv[DP];
+    load_part<D>(K + (size_t)j * D, part, kv);
+    load_part<D>(V + (size_t)j * D, part, vv);
+    float s = dot16<D>(qv, kv) * p.qk_scale;
+    if (j > qc) s = -INFINITY;
+    const float mn = fmaxf(m, s);
+    const float alpha = exp2f(m - mn);
+    const float pj = exp2f(s - mn);
+    l = l * alpha + pj;
+#pragma unroll
+    for (int i = 0; i < DP; ++i) o[i] = fmaf(pj, vv[i], o[i] * alpha);
+    m = mn;
+  }
+  if (q < T_) {
+    const float inv = 1.0f / l;
+    float* orow = p.out + ((size_t)unit * T_ + q) * D + part * DP;
+#pragma unroll
+    for (int i = 0; i < DP; ++i) orow[i] = o[i] * inv;
+    if (part == 0) p.lse2[(size_t)unit * T_ + q] = m + log2f(l);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void colsum_f32_kernel(PrefillParams p) {
+  constexpr int DP = D / 16;
+  const int T_ = p.T;
+  const int kb = blockIdx.x / p.units;
+  const int unit = blockIdx.x - kb * p.units;
+  const int kj = kb * RB + threadIdx.x / 16, part = threadIdx.x % 16;
+  const int kc = kj < T_ ? kj : T_ - 1;
+  const size_t base = (size_t)unit * T_ * D;
+  const float* Q = static_cast<const float*>(p.q) + base;
+  const float* K = static_cast<const float*>(p.k) + base;
+  const float* lse = p.lse2 + (size_t)unit * T_;
+
+  float kv[DP];
+  load_part<D>(K + (size_t)kc * D, part, kv);
+  float cs = 0.f;
+  for (int i = kb * RB; i < T_; ++i) {
+    float qv[DP];
+    load_part<D>(Q + (size_t)i * D, part, qv);
+    const float s = dot16<D>(qv, kv) * p.qk_scale;
+    if (i >= kj) cs += exp2f(s - lse[i]);
+  }
+  if (part == 0 && kj < T_) p.colsum[(size_t)unit * T_ + kj] = cs;
+}
+
+}  // namespace
+
+hipError_t launch_prefill_attn_f32(int D, const PrefillParams& p, hipStream_t s) {
+  const int nqb = (p.T + RB - 1) / RB;
+  const dim3 grid((unsigned)(nqb * p.units));
+  if (D == 64) attn_f32_kernel<64><<<grid, dim3(kThreads), 0, s>>>(p);
+  else attn_f32_kernel<128><<<grid, dim3(kThreads), 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_colsum_f32(int D, const PrefillParams& p, hipStream_t s) {
+  const int nb = (p.T + RB - 1) / RB;
+  const dim3 grid((unsigned)(nb * p.units));
+  if (D == 64) colsum_f32_kernel<64><<<grid, dim3(kThreads), 0, s>>>(p);
+  else colsum_f32_kernel<128><<<grid, dim3(kThreads), 0, s>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace h2o

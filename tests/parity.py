@@ -1,0 +1,141 @@
+"""GPU-vs-oracle parity harness shared by the GPU tests, smoke() and bench.py.
+
+run_gpu() drives the HIP path through the C ABI (via H2OCache) over one layer
+of a workload and keeps every output the oracle can be compared with: prefill
+out and column sums, the cache right after prefill, each decode step's out and
+decision record, and the final cache.
+
+check_units() replays chosen units through the CPU oracle on the exact stored
+inputs and compares element by element:
+  * kept positions / victim slots / slot_pos: bit-exact, except near ties
+    (two candidate fp32 scores within 1e-5 relative), where the oracle adopts
+    the GPU's choice and logs it;
+  * attention outputs: max abs error <= 2e-3 (fp16 / bf16) or 1e-5 (fp32);
+  * scores (acc_score, column sums, evicted scores): 1e-4 relative;
+  * K/V slot rows: bit-exact (they are copies of the inputs).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import UnitCache, decode, prefill
+
+OUT_ATOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 2e-3}
+SCORE_RTOL = 1e-4
+TIE_RTOL = 1e-5
+
+
+def run_gpu(w, x, record_steps=True):
+    from kv_cache_eviction_03_amd import H2OCache
+
+    B, H, d, T, n = w.batch, w.heads, w.head_dim, w.prompt, w.steps
+    dev = x["q_dec"].device if n else x["q_prompt"].device
+    cache = H2OCache(B, H, d, w.k_heavy, w.k_local, w.torch_dtype, dev, max_prompt=T)
+    cache.reset()
+    r = {}
+    if T > 0:
+        r["prefill_out"], r["colsum"] = cache.prefill(x["q_prompt"], x["k_prompt"], x["v_prompt"])
+    else:
+        cache.t = 0
+    r["pos0"] = cache.slot_pos.clone()
+    r["acc0"] = cache.acc_score.clone()
+    if record_steps:
+        r["outs"] = torch.empty((n, B, H, d), dtype=torch.float32, device=dev)
+        r["victims"] = torch.empty((n, B, H), dtype=torch.int32, device=dev)
+        r["ev_pos"] = torch.empty((n, B, H), dtype=torch.int32, device=dev)
+        r["ev_acc"] = torch.empty((n, B, H), dtype=torch.float32, device=dev)
+        for i in range(n):
+            cache.decode(x["q_dec"][i], x["k_dec"][i], x["v_dec"][i], out=r["outs"][i],
+                         victim_slot=r["victims"][i], evicted_pos=r["ev_pos"][i],
+                         evicted_acc=r["ev_acc"][i])
+    torch.cuda.synchronize(dev)
+    r["cache"] = cache
+    return r
+
+
+def unit_inputs(x, b, h):
+    """float64 numpy copies of one unit's exact stored inputs."""
+    f = lambda t: t.double().cpu().numpy()
+    out = {"Qp": f(x["q_prompt"][b, h]), "Kp": f(x["k_prompt"][b, h]), "Vp": f(x["v_prompt"][b, h]),
+           "qd": f(x["q_dec"][:, b, h]), "kd": f(x["k_dec"][:, b, h]), "vd": f(x["v_dec"][:, b, h])}
+    return out
+
+
+def _rel_ok(a, b, rtol):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return np.abs(a - b) <= rtol * np.maximum(np.abs(a), np.abs(b)) + 1e-30
+
+
+def check_unit(w, x, r, b, h, steps=None):
+    """Replay unit (b, h) through the oracle; raise AssertionError on a mismatch.
+
+    Returns a dict of per-unit error figures and the tie log.
+    """
+    atol = OUT_ATOL[w.dtype]
+    T = w.prompt
+    n = w.steps if steps is None else steps
+    u = unit_inputs(x, b, h)
+    pos0 = r["pos0"][b, h].cpu().numpy()
+    acc0 = r["acc0"][b, h].cpu().numpy()
+    cache = UnitCache(w.k_heavy, w.k_local, w.head_dim)
+    err = {"prefill_out": 0.0, "decode_out": 0.0, "colsum_rel": 0.0, "acc_rel": 0.0}
+    if T > 0:
+        kept_gpu = sorted(int(p) for p in pos0 if p >= 0)
+        O, c64 = prefill(cache, u["Qp"], u["Kp"], u["Vp"], adopt_kept=kept_gpu, rel_tol=TIE_RTOL)
+        go = r["prefill_out"][b, h].double().cpu().numpy()
+        err["prefill_out"] = float(np.abs(go - O).max())
+        assert err["prefill_out"] <= atol, f"unit ({b},{h}) prefill out err {err['prefill_out']}"
+        gc = r["colsum"][b, h].double().cpu().numpy()
+        ok = _rel_ok(gc, c64, SCORE_RTOL)
+        err["colsum_rel"] = float((np.abs(gc - c64) / np.maximum(np.abs(c64), 1e-30)).max())
+        assert ok.all(), f"unit ({b},{h}) colsum mismatch at {np.nonzero(~ok)[0][:5]}"
+    assert cache.pos.tolist() == pos0.tolist(), f"unit ({b},{h}) slot_pos after prefill differs"
+    assert _rel_ok(acc0, cache.acc, SCORE_RTOL).all(), f"unit ({b},{h}) acc after prefill differs"
+
+    if n:
+        outs = r["outs"][:n, b, h].double().cpu().numpy()
+        vict = r["victims"][:n, b, h].cpu().numpy()
+        evp = r["ev_pos"][:n, b, h].cpu().numpy()
+        eva = r["ev_acc"][:n, b, h].cpu().numpy()
+        for i in range(n):
+            t = T + i
+            o, v = decode(cache, t, u["qd"][i], u["kd"][i], u["vd"][i],
+                          adopt_victim=int(vict[i]) if vict[i] >= 0 else None, rel_tol=TIE_RTOL)
+            e = float(np.abs(outs[i] - o).max())
+            err["decode_out"] = max(err["decode_out"], e)
+            assert e <= atol, f"unit ({b},{h}) step t={t} out err {e}"
+            assert int(v) == int(vict[i]), f"unit ({b},{h}) t={t}: victim {vict[i]} vs {v}"
+            if v >= 0:
+                _, _, p_ev, a_ev = cache.evictions[-1]
+                assert int(evp[i]) == p_ev, f"unit ({b},{h}) t={t}: evicted pos {evp[i]} vs {p_ev}"
+                assert _rel_ok(eva[i], a_ev, SCORE_RTOL), f"unit ({b},{h}) t={t}: evicted score"
+            else:
+                assert evp[i] == -1
+    gpos = r["cache"].slot_pos[b, h].cpu().numpy()
+    gacc = r["cache"].acc_score[b, h].cpu().numpy()
+    if steps is None or steps == w.steps:
+        assert gpos.tolist() == cache.pos.tolist(), f"unit ({b},{h}) final slot_pos differs"
+        ok = _rel_ok(gacc, cache.acc, SCORE_RTOL)
+        err["acc_rel"] = float((np.abs(gacc - cache.acc) / np.maximum(np.abs(cache.acc), 1e-30)).max())
+        assert ok.all(), f"unit ({b},{h}) final acc differs at slots {np.nonzero(~ok)[0][:5]}"
+        valid = cache.pos >= 0
+        gk = r["cache"].k_slots[b, h].double().cpu().numpy()
+        gv = r["cache"].v_slots[b, h].double().cpu().numpy()
+        assert np.array_equal(gk[valid], cache.K[valid]), f"unit ({b},{h}) K slots differ"
+        assert np.array_equal(gv[valid], cache.V[valid]), f"unit ({b},{h}) V slots differ"
+    err["ties"] = list(cache.ties)
+    return err
+
+
+def check_units(w, x, r, units):
+    """Check a list of flat unit indices (b * H + h). Returns aggregated errors."""
+    agg = {"prefill_out": 0.0, "decode_out": 0.0, "colsum_rel": 0.0, "acc_rel": 0.0, "ties": []}
+    for uidx in units:
+        b, h = divmod(int(uidx), w.heads)
+        e = check_unit(w, x, r, b, h)
+        for k in ("prefill_out", "decode_out", "colsum_rel", "acc_rel"):
+            agg[k] = max(agg[k], e[k])
+        agg["ties"] += [(b, h, *t) for t in e["ties"]]
+    return agg

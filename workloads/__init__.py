@@ -15,7 +15,8 @@ Recipe (all configurations):
   * One torch.Generator on the target device, seeded with
     (seed * 100 + config_id) * 1000 + layer.
   * Draw order: Q for every position, then K, then V, each as fp32 N(0, 1) in
-    position-major chunks of shape [chunk, B, H, d].
+    position-major chunks of shape [chunk, B, H, d], chunk = min(4096,
+    2^24 // (B * H * d)) positions.
   * Heavy-hitter keys (configs with heavy_frac > 0): per sequence, a seeded set of
     round(heavy_frac * (T + n)) positions, shared by every head and layer, plus
     positions 0..sinks-1. For each chosen position j of unit (b, h):
@@ -94,7 +95,7 @@ def generator_seed(w: Workload, seed: int, layer: int) -> int:
 
 @torch.no_grad()
 def generate(w: Workload, seed: int = 0, layer: int = 0, device="cpu",
-             chunk: int = 4096) -> dict:
+             chunk: int | None = None) -> dict:
     """Return the canonical inputs of one layer of workload `w`.
 
     Keys:
@@ -105,6 +106,8 @@ def generate(w: Workload, seed: int = 0, layer: int = 0, device="cpu",
     B, H, d, T, n = w.batch, w.heads, w.head_dim, w.prompt, w.steps
     N = T + n
     dt = w.torch_dtype
+    if chunk is None:   # about 16M draws per call
+        chunk = max(1, min(4096, (1 << 24) // (B * H * d)))
     g = torch.Generator(device=device)
     g.manual_seed(generator_seed(w, seed, layer))
 
@@ -125,15 +128,8 @@ def generate(w: Workload, seed: int = 0, layer: int = 0, device="cpu",
     q_full, q_sum = draw_all()
 
     transform = None
-    count = int(round(w.heavy_frac * N))
-    if count > 0 or w.sinks > 0:
-        gsel = torch.Generator(device="cpu")
-        gsel.manual_seed(generator_seed(w, seed, 999))
-        sel = torch.zeros((B, N), dtype=torch.bool)
-        for b in range(B):
-            if count > 0:
-                sel[b, torch.randperm(N, generator=gsel)[:count]] = True
-            sel[b, :min(w.sinks, N)] = True
+    sel = heavy_positions(w, seed)
+    if bool(sel.any()):
         sel = sel.to(device)
         u = (q_sum / q_sum.norm(dim=-1, keepdim=True)).to(torch.float32)  # [B, H, d]
 
