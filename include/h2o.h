@@ -118,6 +118,13 @@ h2o_status h2o_reset(const h2o_cache_desc* cache, void* stream);
  * h2o_workspace_bytes - device workspace needed by h2o_prefill with prompts of
  * up to max_prompt tokens and by h2o_decode_step on this descriptor's shape.
  * Returns 0 for an invalid descriptor or max_prompt < 0.
+ *
+ * Workspace contract: 256-byte aligned device memory, owned by the caller,
+ * ZERO-FILLED ONCE before its first use. Its leading bytes hold per-unit arrival
+ * counters of the decode step when the decode splits a unit's slots over
+ * several workgroups (large k or few units); every call leaves them zero again.
+ * The rest is scratch whose contents on entry are ignored. One workspace must
+ * not be used by two calls that can run at the same time.
  */
 size_t h2o_workspace_bytes(const h2o_cache_desc* cache, int32_t max_prompt);
 
@@ -131,8 +138,8 @@ size_t h2o_workspace_bytes(const h2o_cache_desc* cache, int32_t max_prompt);
  *               q k^T / sqrt(head_dim) (H2O blog §2.1.1)
  *   colsum_out  NULL or [batch][heads][T] fp32: c_j = sum_{i>=j} P_ij, the
  *               cumulative attention of each prompt token (analysis page §3.1)
- *   workspace   device memory of at least h2o_workspace_bytes(cache, T) bytes,
- *               256-byte aligned; its contents on entry are ignored
+ *   workspace   at least h2o_workspace_bytes(cache, T) bytes (see the workspace
+ *               contract above)
  * Seeding (H2O blog §2.2; analysis page §3.1): if T <= k every position is
  * kept; otherwise the last k_local positions plus the k_heavy positions of
  * [0, T - k_local) with the highest fp32 c_j (ties: the newer position ranks
@@ -152,8 +159,8 @@ h2o_status h2o_prefill(const h2o_cache_desc* cache, const void* q, const void* k
  *   q, k_new, v_new  [batch][heads][head_dim] in dtype, 16-byte aligned
  *   out         [batch][heads][head_dim] fp32, 16-byte aligned
  *   aux         NULL or a host struct of optional device outputs (see above)
- *   workspace   as for h2o_prefill (may be NULL when
- *               h2o_workspace_bytes(cache, 0) is 0)
+ *   workspace   at least h2o_workspace_bytes(cache, 0) bytes (see the
+ *               workspace contract above); may be NULL when that is 0
  * Per unit, with n = min(k, t) valid slots (H2O blog §2.2, §2.3; analysis
  * page §3.2):
  *   1. s_j = q . key_j / sqrt(head_dim) over the n valid slots and the new

@@ -61,8 +61,32 @@ struct ResetParams {
   int64_t n;            // units * k
 };
 
+// Decode launch plan: splits == 0 -> one resident workgroup per unit holding u slot
+// batches; splits > 0 -> `splits` workgroups per unit of kSplitU batches each.
+constexpr int kSplitU = 8;
+struct DecodePlan {
+  int u;
+  int splits;
+};
+DecodePlan plan_decode(int elem_bytes, int D, int k, int units);
+
+// Workspace of the split decode: per-unit arrival counters (zero between calls) and
+// per-split partials plus the step's logits.
+struct SplitScratch {
+  int* counters;        // [units]
+  float* part_ml;       // [units][splits][2]  (max, sum) in the log2 domain
+  float* part_o;        // [units][splits][D]  unnormalised output
+  float* logits;        // [units][k + 1]
+  int splits;
+};
+// Bytes of the scratch part; *counter_bytes receives the size of the counter part.
+size_t decode_scratch_bytes(int elem_bytes, int D, int k, int units, size_t* counter_bytes);
+SplitScratch carve_decode_scratch(int elem_bytes, int D, int k, int units, void* counters,
+                                  void* scratch);
+
 hipError_t launch_reset(const ResetParams& p, hipStream_t s);
-hipError_t launch_decode(DType dt, int D, const DecodeParams& p, hipStream_t s);
+hipError_t launch_decode(DType dt, int D, const DecodeParams& p, const SplitScratch& w,
+                         hipStream_t s);
 // fp16 / bf16 storage: MFMA kernels.
 hipError_t launch_prefill_attn_mfma(DType dt, int D, const PrefillParams& p, hipStream_t s);
 hipError_t launch_prefill_colsum_mfma(DType dt, int D, const PrefillParams& p, hipStream_t s);
@@ -70,8 +94,5 @@ hipError_t launch_prefill_colsum_mfma(DType dt, int D, const PrefillParams& p, h
 hipError_t launch_prefill_attn_f32(int D, const PrefillParams& p, hipStream_t s);
 hipError_t launch_prefill_colsum_f32(int D, const PrefillParams& p, hipStream_t s);
 hipError_t launch_seed(DType dt, int D, const SeedParams& p, hipStream_t s);
-
-// Dynamic LDS bytes the decode kernel needs for k slots.
-size_t decode_lds_bytes(DType dt, int D, int k);
 
 }  // namespace h2o

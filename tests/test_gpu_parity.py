@@ -200,3 +200,15 @@ def test_decode_alone_on_oracle_seeded_cache():
             assert v == vg[0, h]
     for h, u in enumerate(units):
         assert c.slot_pos[0, h].cpu().tolist() == u.pos.tolist()
+
+
+def test_stream_bf16_fill_then_evict_sampled_heads():
+    # The long-streaming shape (4096 slots, no prompt) over the first 6000 steps: 4096
+    # fill steps, then an eviction every step, through the split decode.
+    w = WORKLOADS[5].scaled(steps=6000)
+    announce(f"[parity] {w.name}: k={w.k}, {w.steps} steps, 4 sampled heads")
+    x = gen(w)
+    r = run_gpu(w, x)
+    agg = check_units(w, x, r, [0, 9, 22, 31])
+    announce(f"[parity] {w.name}: decode {agg['decode_out']:.2e} acc {agg['acc_rel']:.2e} "
+             f"ties={len(agg['ties'])}")
