@@ -23,6 +23,9 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # Keep the compiler from forming packed fp32 VALU ops (v_pk_*_f32).
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: the softmax reads them every tile, and the AGPR form
+    # costs a v_accvgpr copy per element each way.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
     f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
 ]

@@ -137,7 +137,7 @@ __global__ __launch_bounds__(kThreads) void decode_resident_kernel(DecodeParams 
   __shared__ __attribute__((aligned(16))) float s_red[ROWS * D];
   __shared__ float s_m[ROWS], s_l[ROWS];
   __shared__ float s_logit[ROWS * U];
-  __shared__ uint64_t s_key[kWaves];
+  __shared__ unsigned long long s_best;
 
   const int unit = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -163,6 +163,7 @@ __global__ __launch_bounds__(kThreads) void decode_resident_kernel(DecodeParams 
   const int jc = own ? jo : 0;
   const float acc_old = acc[jc];
   const int pos_old = pos[jc];
+  if (tid == 0) s_best = ~0ull;
   __builtin_amdgcn_sched_barrier(0);            // keep every load ahead of the math
 
   float s[U], mg, lg, o[VEC];
@@ -203,14 +204,13 @@ __global__ __launch_bounds__(kThreads) void decode_resident_kernel(DecodeParams 
   if (own) {
     a = acc_old + exp2f(s_logit[jo] - M) * inv;
     acc[jo] = a;
-    if (full && pos_old <= limit) key = score_key(a, pos_old);
+    if (full && pos_old <= limit) {
+      key = score_key(a, pos_old);
+      atomicMin(&s_best, (unsigned long long)key);   // order-independent minimum
+    }
   }
-  const uint64_t wmin = wave_min_u64(key);
-  if (lane == 0) s_key[wave] = wmin;
   __syncthreads();                              // (2)
-  uint64_t best = s_key[0];
-#pragma unroll
-  for (int w = 1; w < kWaves; ++w) best = s_key[w] < best ? s_key[w] : best;
+  const uint64_t best = s_best;
 
   int dst = -1;
   bool meta = false;
@@ -245,7 +245,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p, 
   constexpr int C = ROWS * U;                   // slots per workgroup
   __shared__ __attribute__((aligned(16))) float s_red[ROWS * D];
   __shared__ float s_m[ROWS], s_l[ROWS];
-  __shared__ uint64_t s_key[kWaves];
+  __shared__ unsigned long long s_best;
   __shared__ int s_last, s_dst;
 
   const int nsplit = w.splits;
@@ -333,6 +333,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p, 
     p.out[(size_t)unit * D + c] = v * inv;
   }
   const float p_new = exp2f(logit[n] - M) * inv;
+  if (tid == 0) {
+    s_best = ~0ull;
+    s_dst = full ? -1 : n;
+  }
+  __syncthreads();
 
   uint64_t best = ~0ull;
   int best_slot = -1;
@@ -345,13 +350,9 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p, 
       if (key < best) { best = key; best_slot = j; }
     }
   }
-  const uint64_t wmin = wave_min_u64(best);
-  if (lane == 0) s_key[wave] = wmin;
-  if (tid == 0) s_dst = full ? -1 : n;
+  if (best_slot >= 0) atomicMin(&s_best, (unsigned long long)best);
   __syncthreads();
-  uint64_t gbest = s_key[0];
-#pragma unroll
-  for (int q = 1; q < kWaves; ++q) gbest = s_key[q] < gbest ? s_key[q] : gbest;
+  const uint64_t gbest = s_best;
   const bool mine = full && best_slot >= 0 && best == gbest;
   if (mine) s_dst = best_slot;
   __syncthreads();

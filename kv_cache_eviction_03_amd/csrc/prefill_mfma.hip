@@ -17,6 +17,11 @@
 // directly as the B operand (no LDS round trip), and the output accumulators
 // again belong to query l%16, so the online rescale is lane-local.
 //
+// Tiling: each wave holds RB blocks of 16 rows, so every operand read from LDS
+// feeds RB MFMAs; the next key (or query) tile is loaded into registers while
+// the current one is consumed from LDS. LDS row strides are padded so that the
+// 16-byte K reads and the 8-byte V^T reads and writes are bank-conflict free.
+//
 // bf16: P rounded to bf16 alone gives up to ~3e-3 abs error on O for N(0,1)
 // data, so P is split into a bf16 high part and a bf16 residual, two MFMAs.
 #include "h2o_device.hpp"
@@ -25,41 +30,80 @@
 namespace h2o {
 namespace {
 
-constexpr int BM = 64;    // query rows per workgroup (16 per wave)
-constexpr int BN = 64;    // keys per tile
+constexpr int BN = 64;    // keys per tile (attention) / queries per tile (column sums)
+constexpr float kLazy = 8.f;  // log2-domain slack before the running max is moved
 constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
 
 template <typename T> __device__ __forceinline__ typename Vec8<T>::type ld8(const T* p) {
   return *reinterpret_cast<const typename Vec8<T>::type*>(p);
 }
 
-// Cooperative K tile load: BN rows x D into LDS rows of stride D + 8.
-template <typename T, int D>
-__device__ __forceinline__ void load_rows(T* tile, const T* src, int row0, int T_, int tid) {
-  constexpr int CPR = D / 8;  // 16-byte chunks per row
-  constexpr int KS = D + 8;
-#pragma unroll
-  for (int c = tid; c < BN * CPR; c += kThreads) {
-    const int row = c / CPR, cc = c % CPR;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (row0 + row < T_) v = ld16(src + (size_t)(row0 + row) * D + cc * 8);
-    st16(tile + row * KS + cc * 8, v);
-  }
-}
+template <int D> struct Tile {
+  static constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  static constexpr int KS = D + 8;                   // row-major tile stride (elements)
+  static constexpr int VS = BN + 4;                  // V^T stride: 34 dwords per row
+  static constexpr int KCH = BN * CPR / kThreads;    // row chunks per thread
+  static constexpr int VBL = (BN / 4) * CPR;         // 4-key x 8-dim blocks of V
+};
 
-// Cooperative V tile load, transposed: LDS holds V^T [D][BN + 8].
+// One BN-row tile of a [T][D] matrix, held in registers between the global load
+// and the LDS store. Rows past T are loaded from row T-1 and zeroed.
 template <typename T, int D>
-__device__ __forceinline__ void load_vt(T* tile, const T* src, int row0, int T_, int tid) {
-  constexpr int CPR = D / 8;
-  constexpr int VS = BN + 8;
-  for (int c = tid; c < (BN / 4) * CPR; c += kThreads) {
-    const int kg = c / CPR, dc = c % CPR;
-    uint4 r[4];
+struct RowTile {
+  uint4 c[Tile<D>::KCH];
+  __device__ __forceinline__ void load(const T* src, int row0, int T_, int tid) {
+    if (row0 + BN <= T_) {                       // whole tile in range
+#pragma unroll
+      for (int i = 0; i < Tile<D>::KCH; ++i) {
+        const int ch = tid + i * kThreads, row = ch / Tile<D>::CPR, cc = ch % Tile<D>::CPR;
+        c[i] = ld16(src + (size_t)(row0 + row) * D + cc * 8);
+      }
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < Tile<D>::KCH; ++i) {
+      const int ch = tid + i * kThreads, row = ch / Tile<D>::CPR, cc = ch % Tile<D>::CPR;
+      const int r = row0 + row;
+      uint4 v = ld16(src + (size_t)(r < T_ ? r : T_ - 1) * D + cc * 8);
+      if (r >= T_) v = make_uint4(0, 0, 0, 0);
+      c[i] = v;
+    }
+  }
+  __device__ __forceinline__ void store(T* tile, int tid) const {
+#pragma unroll
+    for (int i = 0; i < Tile<D>::KCH; ++i) {
+      const int ch = tid + i * kThreads, row = ch / Tile<D>::CPR, cc = ch % Tile<D>::CPR;
+      st16(tile + row * Tile<D>::KS + cc * 8, c[i]);
+    }
+  }
+};
+
+// A V tile for the transposed LDS copy: thread tid < VBL holds keys 4kg..4kg+3 of
+// dims 8dc..8dc+7, kg fastest across lanes so the transposed 8-byte writes of a
+// 16-lane group are contiguous.
+template <typename T, int D>
+struct VTile {
+  uint4 r[4];
+  __device__ __forceinline__ void load(const T* src, int row0, int T_, int tid) {
+    if (tid >= Tile<D>::VBL) return;
+    const int kg = tid % (BN / 4), dc = tid / (BN / 4);
+    if (row0 + BN <= T_) {                       // whole tile in range
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = ld16(src + (size_t)(row0 + 4 * kg + e) * D + dc * 8);
+      return;
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int key = row0 + 4 * kg + e;
-      r[e] = key < T_ ? ld16(src + (size_t)key * D + dc * 8) : make_uint4(0, 0, 0, 0);
+      uint4 v = ld16(src + (size_t)(key < T_ ? key : T_ - 1) * D + dc * 8);
+      if (key >= T_) v = make_uint4(0, 0, 0, 0);
+      r[e] = v;
     }
+  }
+  __device__ __forceinline__ void store(T* tile, int tid) const {
+    if (tid >= Tile<D>::VBL) return;
+    const int kg = tid % (BN / 4), dc = tid / (BN / 4);
     const uint32_t w[4][4] = {{r[0].x, r[0].y, r[0].z, r[0].w}, {r[1].x, r[1].y, r[1].z, r[1].w},
                               {r[2].x, r[2].y, r[2].z, r[2].w}, {r[3].x, r[3].y, r[3].z, r[3].w}};
 #pragma unroll
@@ -68,17 +112,18 @@ __device__ __forceinline__ void load_vt(T* tile, const T* src, int row0, int T_,
       uint2 o;
       o.x = ((w[0][word] >> sh) & 0xffffu) | (((w[1][word] >> sh) & 0xffffu) << 16);
       o.y = ((w[2][word] >> sh) & 0xffffu) | (((w[3][word] >> sh) & 0xffffu) << 16);
-      *reinterpret_cast<uint2*>(tile + (dc * 8 + e8) * VS + 4 * kg) = o;
+      *reinterpret_cast<uint2*>(tile + (dc * 8 + e8) * Tile<D>::VS + 4 * kg) = o;
     }
   }
-}
+};
 
-template <typename T, int D>
+template <typename T, int D, int RB, bool PREFETCH>
 __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p) {
   using V8 = typename Vec8<T>::type;
   using V4 = typename Vec8<T>::half;
-  constexpr bool kSplit = sizeof(T) == 2 && !__is_same(T, _Float16);
-  constexpr int KS = D + 8, VS = BN + 8;
+  constexpr bool kSplit = !__is_same(T, _Float16);
+  constexpr int BM = kWaves * 16 * RB;
+  constexpr int KS = Tile<D>::KS, VS = Tile<D>::VS;
   __shared__ __attribute__((aligned(16))) T k_tile[BN * KS];
   __shared__ __attribute__((aligned(16))) T v_tile[D * VS];
 
@@ -93,113 +138,182 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p)
   const T* Q = static_cast<const T*>(p.q) + base;
   const T* K = static_cast<const T*>(p.k) + base;
   const T* V = static_cast<const T*>(p.v) + base;
-  const int qrow = qb * BM + wave * 16 + l16;
+  const int row0 = qb * BM + wave * 16 * RB;    // this wave's first row
 
-  V8 qa[D / 32];
+  V8 qa[RB][D / 32];
 #pragma unroll
-  for (int kk = 0; kk < D / 32; ++kk) {
-    V8 z = {};
-    qa[kk] = qrow < T_ ? ld8(Q + (size_t)qrow * D + kk * 32 + 8 * g) : z;
+  for (int rb = 0; rb < RB; ++rb) {
+    const int qr = row0 + rb * 16 + l16;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      V8 v = ld8(Q + (size_t)(qr < T_ ? qr : T_ - 1) * D + kk * 32 + 8 * g);
+      if (qr >= T_) v = V8{};
+      qa[rb][kk] = v;
+    }
   }
 
-  f32x4 o[D / 16];
+  f32x4 o[RB][D / 16];
+  float m[RB], ls[RB];
 #pragma unroll
-  for (int db = 0; db < D / 16; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, lsum = 0.f;
+  for (int rb = 0; rb < RB; ++rb) {
+    m[rb] = -INFINITY;
+    ls[rb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
-  for (int kt = 0; kt <= qb; ++kt) {
+  const int kend = min(T_, (qb + 1) * BM);
+  const int nkt = (kend + BN - 1) / BN;
+  RowTile<T, D> kreg;
+  VTile<T, D> vreg;
+  if constexpr (PREFETCH) {
+    kreg.load(K, 0, T_, tid);
+    vreg.load(V, 0, T_, tid);
+  }
+
+  for (int kt = 0; kt < nkt; ++kt) {
     const int key0 = kt * BN;
-    load_rows<T, D>(k_tile, K, key0, T_, tid);
-    load_vt<T, D>(v_tile, V, key0, T_, tid);
-    __syncthreads();
-
-    f32x4 s[BN / 16];
-#pragma unroll
-    for (int kb = 0; kb < BN / 16; ++kb) {
-      s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk)
-        s[kb] = mfma16x16x32(ld8(k_tile + (kb * 16 + l16) * KS + kk * 32 + 8 * g), qa[kk], s[kb]);
+    if constexpr (PREFETCH) {
+      kreg.store(k_tile, tid);
+      vreg.store(v_tile, tid);
+      __syncthreads();
+      if (kt + 1 < nkt) {
+        kreg.load(K, key0 + BN, T_, tid);
+        vreg.load(V, key0 + BN, T_, tid);
+      }
+      __builtin_amdgcn_sched_barrier(0);        // next tile's loads go out first
+    } else {
+      kreg.load(K, key0, T_, tid);
+      vreg.load(V, key0, T_, tid);
+      kreg.store(k_tile, tid);
+      vreg.store(v_tile, tid);
+      __syncthreads();
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < BN / 16; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = key0 + kb * 16 + 4 * g + i;
-        float x = s[kb][i] * p.qk_scale;
-        if (key > qrow || key >= T_) x = -INFINITY;
-        s[kb][i] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    const float mnew = fmaxf(m, mx);
-    const float alpha = exp2f(m - mnew);
-    m = mnew;
-    float ps = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < BN / 16; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x = exp2f(s[kb][i] - mnew);
-        s[kb][i] = x;
-        ps += x;
-      }
-    lsum = lsum * alpha + ps;
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db) o[db] *= alpha;
+    // Only tiles that reach past the wave's first row need the causal mask.
+    const bool diag = key0 + BN - 1 > row0 || key0 + BN > T_;
 
-    V8 pb[BN / 32], pl[BN / 32];
+    f32x4 s[RB][BN / 16];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int kb = 0; kb < BN / 16; ++kb) s[rb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {       // consecutive MFMAs use different accumulators
+      V8 a[BN / 16];
+#pragma unroll
+      for (int kb = 0; kb < BN / 16; ++kb) a[kb] = ld8(k_tile + (kb * 16 + l16) * KS + kk * 32 + 8 * g);
+#pragma unroll
+      for (int kb = 0; kb < BN / 16; ++kb)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) s[rb][kb] = mfma16x16x32(a[kb], qa[rb][kk], s[rb][kb]);
+    }
+
+    // Online softmax in the log2 domain with the 1/sqrt(d) scale folded into one FMA
+    // per logit. The running max only moves when a row's new max exceeds it by more
+    // than kLazy (checked per wave), so most tiles skip the output rescale; P then
+    // stays <= 2^kLazy, well inside fp16/bf16 range.
+    V8 pb[RB][BN / 32], pl[RB][BN / 32];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int qrow = row0 + rb * 16 + l16;
+      float mx = -INFINITY;
+      if (diag) {
+#pragma unroll
+        for (int kb = 0; kb < BN / 16; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = key0 + kb * 16 + 4 * g + i;
+            if (key > qrow || key >= T_) s[rb][kb][i] = -INFINITY;
+            mx = fmaxf(mx, s[rb][kb][i]);
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < BN / 16; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[rb][kb][i]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      const float mt = mx * p.qk_scale;
+      const bool grow = mt > m[rb] + kLazy;
+      if (__any(grow)) {
+        const float mnew = grow ? mt : m[rb];
+        const float alpha = exp2f(m[rb] - mnew);
+        m[rb] = mnew;
+        ls[rb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) o[rb][db] *= alpha;
+      }
+      const float nm = -m[rb];
+      float ps = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < BN / 16; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x = exp2f(fmaf(s[rb][kb][i], p.qk_scale, nm));
+          s[rb][kb][i] = x;
+          ps += x;
+        }
+      ls[rb] += ps;
+#pragma unroll
+      for (int ks = 0; ks < BN / 32; ++ks)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pb[rb][ks][i] = (T)s[rb][2 * ks][i];
+          pb[rb][ks][4 + i] = (T)s[rb][2 * ks + 1][i];
+          if constexpr (kSplit) {
+            pl[rb][ks][i] = (T)(s[rb][2 * ks][i] - (float)pb[rb][ks][i]);
+            pl[rb][ks][4 + i] = (T)(s[rb][2 * ks + 1][i] - (float)pb[rb][ks][4 + i]);
+          }
+        }
+    }
+
 #pragma unroll
     for (int ks = 0; ks < BN / 32; ++ks)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pb[ks][i] = (T)s[2 * ks][i];
-        pb[ks][4 + i] = (T)s[2 * ks + 1][i];
-        if constexpr (kSplit) {
-          pl[ks][i] = (T)(s[2 * ks][i] - (float)pb[ks][i]);
-          pl[ks][4 + i] = (T)(s[2 * ks + 1][i] - (float)pb[ks][4 + i]);
-        }
-      }
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-      for (int ks = 0; ks < BN / 32; ++ks) {
+      for (int db = 0; db < D / 16; ++db) {
         const T* vr = v_tile + (db * 16 + l16) * VS + ks * 32 + 4 * g;
         const V4 lo = *reinterpret_cast<const V4*>(vr);
         const V4 hi = *reinterpret_cast<const V4*>(vr + 16);
         const V8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[db] = mfma16x16x32(a, pb[ks], o[db]);
-        if constexpr (kSplit) o[db] = mfma16x16x32(a, pl[ks], o[db]);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          o[rb][db] = mfma16x16x32(a, pb[rb][ks], o[rb][db]);
+          if constexpr (kSplit) o[rb][db] = mfma16x16x32(a, pl[rb][ks], o[rb][db]);
+        }
       }
     __syncthreads();
   }
 
-  float lt = lsum + __shfl_xor(lsum, 16, kWave);
-  lt = lt + __shfl_xor(lt, 32, kWave);
-  if (qrow < T_) {
-    const float inv = 1.0f / lt;
-    float* orow = p.out + ((size_t)unit * T_ + qrow) * D;
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db) {
-      const f32x4 v = o[db] * inv;
-      *reinterpret_cast<f32x4*>(orow + db * 16 + 4 * g) = v;
+  for (int rb = 0; rb < RB; ++rb) {
+    const int qrow = row0 + rb * 16 + l16;
+    float lt = ls[rb] + __shfl_xor(ls[rb], 16, kWave);
+    lt = lt + __shfl_xor(lt, 32, kWave);
+    if (qrow < T_) {
+      const float inv = 1.0f / lt;
+      float* orow = p.out + ((size_t)unit * T_ + qrow) * D;
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        const f32x4 v = o[rb][db] * inv;
+        *reinterpret_cast<f32x4*>(orow + db * 16 + 4 * g) = v;
+      }
+      if (g == 0) p.lse2[(size_t)unit * T_ + qrow] = m[rb] + log2f(lt);
     }
-    if (g == 0) p.lse2[(size_t)unit * T_ + qrow] = m + log2f(lt);
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, int RB, bool PREFETCH>
 __global__ __launch_bounds__(kThreads) void prefill_colsum_kernel(PrefillParams p) {
   using V8 = typename Vec8<T>::type;
-  constexpr int KS = D + 8;
-  __shared__ __attribute__((aligned(16))) T q_tile[BM * KS];
-  __shared__ float lse_tile[BM];
+  constexpr int BK = kWaves * 16 * RB;          // keys per workgroup
+  constexpr int KS = Tile<D>::KS;
+  __shared__ __attribute__((aligned(16))) T q_tile[BN * KS];
+  __shared__ float lse_tile[BN];
 
   const int T_ = p.T;
-  const int nb = (T_ + BN - 1) / BN;
-  const int kb = blockIdx.x / p.units;         // early keys (most rows) first
+  const int nq = (T_ + BN - 1) / BN;
+  const int kb = blockIdx.x / p.units;          // early keys (most rows) first
   const int unit = blockIdx.x - kb * p.units;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
@@ -207,58 +321,129 @@ __global__ __launch_bounds__(kThreads) void prefill_colsum_kernel(PrefillParams 
   const T* Q = static_cast<const T*>(p.q) + base;
   const T* K = static_cast<const T*>(p.k) + base;
   const float* lse = p.lse2 + (size_t)unit * T_;
-  const int key0 = kb * BN + wave * 16;        // this wave's 16 keys
+  const int key0 = kb * BK + wave * 16 * RB;    // this wave's first key
 
-  V8 ka[D / 32];
+  V8 ka[RB][D / 32];
 #pragma unroll
-  for (int kk = 0; kk < D / 32; ++kk) {
-    V8 z = {};
-    ka[kk] = key0 + l16 < T_ ? ld8(K + (size_t)(key0 + l16) * D + kk * 32 + 8 * g) : z;
+  for (int rb = 0; rb < RB; ++rb) {
+    const int kr = key0 + rb * 16 + l16;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      V8 v = ld8(K + (size_t)(kr < T_ ? kr : T_ - 1) * D + kk * 32 + 8 * g);
+      if (kr >= T_) v = V8{};
+      ka[rb][kk] = v;
+    }
   }
-  float cs[4] = {0.f, 0.f, 0.f, 0.f};
+  float cs[RB][4];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cs[rb][i] = 0.f;
 
-  for (int qt = kb; qt < nb; ++qt) {
-    const int q0 = qt * BM;
-    load_rows<T, D>(q_tile, Q, q0, T_, tid);
-    if (tid < BM) lse_tile[tid] = q0 + tid < T_ ? lse[q0 + tid] : 0.f;
-    __syncthreads();
-#pragma unroll
-    for (int qb = 0; qb < BM / 16; ++qb) {
-      f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk)
-        s = mfma16x16x32(ka[kk], ld8(q_tile + (qb * 16 + l16) * KS + kk * 32 + 8 * g), s);
-      const int q = q0 + qb * 16 + l16;
-      const float l2 = lse_tile[qb * 16 + l16];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = key0 + 4 * g + i;
-        if (q < T_ && q >= key) cs[i] += exp2f(s[i] * p.qk_scale - l2);
+  const int qt0 = (kb * BK) / BN;
+  RowTile<T, D> qreg;
+  float lreg = 0.f;
+  if constexpr (PREFETCH) {
+    qreg.load(Q, qt0 * BN, T_, tid);
+    if (tid < BN) lreg = qt0 * BN + tid < T_ ? lse[qt0 * BN + tid] : 0.f;
+  }
+
+  for (int qt = qt0; qt < nq; ++qt) {
+    const int q0 = qt * BN;
+    if constexpr (PREFETCH) {
+      qreg.store(q_tile, tid);
+      if (tid < BN) lse_tile[tid] = lreg;
+      __syncthreads();
+      if (qt + 1 < nq) {
+        qreg.load(Q, q0 + BN, T_, tid);
+        if (tid < BN) lreg = q0 + BN + tid < T_ ? lse[q0 + BN + tid] : 0.f;
       }
+      __builtin_amdgcn_sched_barrier(0);        // next tile's loads go out first
+    } else {
+      qreg.load(Q, q0, T_, tid);
+      if (tid < BN) lreg = q0 + tid < T_ ? lse[q0 + tid] : 0.f;
+      qreg.store(q_tile, tid);
+      if (tid < BN) lse_tile[tid] = lreg;
+      __syncthreads();
+    }
+    const bool diag = q0 < key0 + 16 * RB;      // some queries of the tile precede some keys
+    f32x4 s[BN / 16][RB];
+#pragma unroll
+    for (int qb = 0; qb < BN / 16; ++qb)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) s[qb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {       // consecutive MFMAs use different accumulators
+      V8 b[BN / 16];
+#pragma unroll
+      for (int qb = 0; qb < BN / 16; ++qb) b[qb] = ld8(q_tile + (qb * 16 + l16) * KS + kk * 32 + 8 * g);
+#pragma unroll
+      for (int qb = 0; qb < BN / 16; ++qb)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) s[qb][rb] = mfma16x16x32(ka[rb][kk], b[qb], s[qb][rb]);
+    }
+    const bool masked = diag || q0 + BN > T_;
+#pragma unroll
+    for (int qb = 0; qb < BN / 16; ++qb) {
+      const int q = q0 + qb * 16 + l16;
+      const float nl = -lse_tile[qb * 16 + l16];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = exp2f(fmaf(s[qb][rb][i], p.qk_scale, nl));
+          if (masked) {
+            const int key = key0 + rb * 16 + 4 * g + i;
+            cs[rb][i] += (q < T_ && q >= key) ? e : 0.f;
+          } else {
+            cs[rb][i] += e;
+          }
+        }
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) cs[i] = group_sum<16>(cs[i]);
-  if (l16 == 0) {
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int key = key0 + 4 * g + i;
-      if (key < T_) p.colsum[(size_t)unit * T_ + key] = cs[i];
+      const float v = group_sum<16>(cs[rb][i]);
+      const int key = key0 + rb * 16 + 4 * g + i;
+      if (l16 == 0 && key < T_) p.colsum[(size_t)unit * T_ + key] = v;
     }
-  }
 }
+
+// Tuning knobs (compile-time): 16-row blocks per wave and register prefetch of the
+// next tile, for the attention and the column-sum kernels.
+// Defaults from a sweep on MI355X (OPT-30B-shaped prompt, T = 2048): attention
+// 2.06 ms with RB = 2 + prefetch vs 3.2 ms with RB = 1; column sums 1.11 ms with
+// RB = 2 and no prefetch.
+#ifndef H2O_ATTN_RB
+#define H2O_ATTN_RB 2
+#endif
+#ifndef H2O_ATTN_PREFETCH
+#define H2O_ATTN_PREFETCH 1
+#endif
+#ifndef H2O_COLSUM_RB
+#define H2O_COLSUM_RB 2
+#endif
+#ifndef H2O_COLSUM_PREFETCH
+#define H2O_COLSUM_PREFETCH 0
+#endif
 
 template <typename T, int D>
 hipError_t attn(const PrefillParams& p, hipStream_t s) {
+  constexpr int BM = kWaves * 16 * H2O_ATTN_RB;
   const int nqb = (p.T + BM - 1) / BM;
-  prefill_attn_kernel<T, D><<<dim3((unsigned)(nqb * p.units)), dim3(kThreads), 0, s>>>(p);
+  prefill_attn_kernel<T, D, H2O_ATTN_RB, H2O_ATTN_PREFETCH != 0>
+      <<<dim3((unsigned)(nqb * p.units)), dim3(kThreads), 0, s>>>(p);
   return hipGetLastError();
 }
 template <typename T, int D>
 hipError_t colsum(const PrefillParams& p, hipStream_t s) {
-  const int nb = (p.T + BN - 1) / BN;
-  prefill_colsum_kernel<T, D><<<dim3((unsigned)(nb * p.units)), dim3(kThreads), 0, s>>>(p);
+  constexpr int BK = kWaves * 16 * H2O_COLSUM_RB;
+  const int nb = (p.T + BK - 1) / BK;
+  prefill_colsum_kernel<T, D, H2O_COLSUM_RB, H2O_COLSUM_PREFETCH != 0>
+      <<<dim3((unsigned)(nb * p.units)), dim3(kThreads), 0, s>>>(p);
   return hipGetLastError();
 }
 

@@ -4,12 +4,17 @@
 // the H2O blog, ttsmallhot.github.io, §2.2) plus the k_heavy positions of
 // [0, T - k_local) with the highest fp32 column sum, i.e. the top-k of the
 // cumulative attention ("H2O Heavy-Hitter Oracle 分析", §3.1). Ties rank the
-// newer position higher, so the older one is dropped. The k_heavy-th largest
-// 64-bit key (float bits of c_j << 32 | j; c_j >= 0 so the bits order like the
-// values) is found by an 8-pass MSB radix select over LDS histograms, which
-// needs O(1) LDS for any prompt length; kept positions are then compacted in
-// ascending order with a ballot scan and their K/V rows copied into slots.
-// If T <= k every position is kept. Slots past the kept count are marked free.
+// newer position higher, so the older one is dropped. If T <= k every
+// position is kept. Kept positions fill slots 0.. in ascending order; the
+// other slots are marked free.
+//
+// Selection: column sums are >= 0, so their fp32 bit patterns order like the
+// values. Four MSB-first radix passes (8-bit digits, 256-bin LDS histogram, a
+// wave-level scan of the bins) find the k_heavy-th largest bit pattern v* and
+// how many positions equal to v* must be kept. One ordered ballot sweep over
+// the positions then keeps every candidate above v*, the newest of those equal
+// to v*, and the recent window, writing kept positions to slots in order.
+// Column sums are staged in LDS when they fit (T + k <= 15872 words).
 //
 // reset: slot_pos = -1, acc = 0 (blog §2.3: freeing a slot only marks it).
 #include "h2o_device.hpp"
@@ -19,23 +24,36 @@ namespace h2o {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+// Column sums are staged in LDS when slot table + sums fit in 62 KB of dynamic LDS.
+constexpr int kStageWords = 62 * 1024 / 4;
+__host__ __device__ inline bool stage_bits(int T, int k) { return T > k && T + k <= kStageWords; }
 
-__device__ __forceinline__ uint64_t seed_key(const float* c, int j) {
-  return ((uint64_t)__float_as_uint(c[j]) << 32) | (uint32_t)j;
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ unsigned wave_prefix(unsigned v, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const unsigned u = __shfl_up(v, o, kWave);
+    if (lane >= o) v += u;
+  }
+  return v;
 }
 
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void seed_kernel(SeedParams p) {
-  extern __shared__ int slot_of[];               // [k] position held by each kept slot
+  extern __shared__ int lds_dyn[];               // [k] slot -> position, then [T] staged bits
   __shared__ unsigned hist[256];
-  __shared__ unsigned suf[256];
+  __shared__ unsigned wsum[kWaves];
   __shared__ unsigned s_sel, s_above;
-  __shared__ int wcount[kThreads / kWave];
+  __shared__ int wcnt[2][kWaves];
 
   const int unit = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int T_ = p.T, k = p.k_heavy + p.k_local;
   const float* c = p.colsum + (size_t)unit * T_;
+  int* slot_of = lds_dyn;
+  unsigned* bits = reinterpret_cast<unsigned*>(lds_dyn + k);
+  const bool staged = stage_bits(T_, k);
 
   int n_keep;
   if (T_ <= k) {
@@ -43,50 +61,81 @@ __global__ __launch_bounds__(kThreads) void seed_kernel(SeedParams p) {
     for (int s = tid; s < T_; s += kThreads) slot_of[s] = s;
   } else {
     const int ncand = T_ - p.k_local;
-    uint64_t thr = ~0ull;                         // no heavy hitter passes ~0
+    if (staged)
+      for (int j = tid; j < ncand; j += kThreads) bits[j] = __float_as_uint(c[j]);
+    auto key = [&](int j) -> unsigned { return staged ? bits[j] : __float_as_uint(c[j]); };
+
+    unsigned prefix = 0, mask = 0, want = (unsigned)p.k_heavy, eq_total = 0;
     if (p.k_heavy > 0) {
-      uint64_t prefix = 0, mask = 0;
-      unsigned want = (unsigned)p.k_heavy;        // rank from the top, 1-based
-      for (int pass = 7; pass >= 0; --pass) {
+      for (int pass = 3; pass >= 0; --pass) {
         const int sh = pass * 8;
         hist[tid] = 0;
         __syncthreads();
         for (int j = tid; j < ncand; j += kThreads) {
-          const uint64_t key = seed_key(c, j);
-          if ((key & mask) == prefix) atomicAdd(&hist[(key >> sh) & 255u], 1u);
+          const unsigned b = key(j);
+          if ((b & mask) == prefix) atomicAdd(&hist[(b >> sh) & 255u], 1u);
         }
         __syncthreads();
-        suf[tid] = hist[tid];
+        // Thread i holds bin 255 - i, so a prefix over threads is a suffix over bins.
+        const unsigned cnt = hist[255 - tid];
+        const unsigned incl_w = wave_prefix(cnt, lane);
+        if (lane == 63) wsum[wave] = incl_w;
         __syncthreads();
-        for (int off = 1; off < 256; off <<= 1) {
-          const unsigned add = tid + off < 256 ? suf[tid + off] : 0u;
-          __syncthreads();
-          suf[tid] += add;
-          __syncthreads();
+        unsigned before = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) before += w < wave ? wsum[w] : 0u;
+        const unsigned incl = before + incl_w, excl = incl - cnt;
+        if (excl < want && want <= incl) {       // exactly one bin qualifies
+          s_sel = 255u - (unsigned)tid;
+          s_above = excl;
         }
-        const unsigned here = suf[tid], next = tid < 255 ? suf[tid + 1] : 0u;
-        if (here >= want && next < want) { s_sel = (unsigned)tid; s_above = next; }
         __syncthreads();
-        prefix |= (uint64_t)s_sel << sh;
-        mask |= 255ull << sh;
+        prefix |= s_sel << sh;
+        mask |= 255u << sh;
         want -= s_above;
+        if (pass == 0) eq_total = hist[s_sel];
         __syncthreads();
       }
-      thr = prefix;                              // exactly k_heavy keys are >= thr
     }
-    int running = 0;
+    // Keep: j >= ncand (recent window); bits > v*; bits == v* and among the `want`
+    // newest such positions (want = how many equal ones are still needed).
+    const unsigned vstar = prefix;
+    const bool any_heavy = p.k_heavy > 0;
+    int running = 0, eq_seen = 0;
     for (int base = 0; base < T_; base += kThreads) {
       const int j = base + tid;
-      const bool keep = j < T_ && (j >= ncand || seed_key(c, j) >= thr);
-      const uint64_t b = __ballot(keep);
-      const int in_wave = __popcll(b & ((1ull << lane) - 1ull));
-      if (lane == 0) wcount[wave] = __popcll(b);
+      bool keep = false, eq = false;
+      if (j < T_) {
+        if (j >= ncand) {
+          keep = true;
+        } else if (any_heavy) {
+          const unsigned b = key(j);
+          eq = b == vstar;
+          keep = b > vstar;
+        }
+      }
+      const uint64_t beq = __ballot(eq);
+      const int eq_in_wave = __popcll(beq & ((1ull << lane) - 1ull));
+      if (lane == 0) wcnt[1][wave] = __popcll(beq);
+      // Position index among equal keys decides whether this one is among the newest.
+      __syncthreads();
+      int eq_off = 0, eq_tot = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        eq_off += w < wave ? wcnt[1][w] : 0;
+        eq_tot += wcnt[1][w];
+      }
+      if (eq && eq_seen + eq_off + eq_in_wave >= (int)eq_total - (int)want) keep = true;
+      eq_seen += eq_tot;
+      const uint64_t bk = __ballot(keep);
+      const int in_wave = __popcll(bk & ((1ull << lane) - 1ull));
+      if (lane == 0) wcnt[0][wave] = __popcll(bk);
       __syncthreads();
       int off = 0, total = 0;
 #pragma unroll
-      for (int w = 0; w < kThreads / kWave; ++w) {
-        off += w < wave ? wcount[w] : 0;
-        total += wcount[w];
+      for (int w = 0; w < kWaves; ++w) {
+        off += w < wave ? wcnt[0][w] : 0;
+        total += wcnt[0][w];
       }
       if (keep && running + off + in_wave < k) slot_of[running + off + in_wave] = j;
       running += total;
@@ -110,15 +159,32 @@ __global__ __launch_bounds__(kThreads) void seed_kernel(SeedParams p) {
   }
   constexpr int CPR = D * (int)sizeof(T) / 16;   // 16-byte chunks per row
   constexpr int VEC = 16 / (int)sizeof(T);
+  constexpr int B = 4;                           // copies in flight per thread
   const T* K = static_cast<const T*>(p.k) + (size_t)unit * T_ * D;
   const T* V = static_cast<const T*>(p.v) + (size_t)unit * T_ * D;
   T* ks = static_cast<T*>(p.k_slots) + (size_t)unit * k * D;
   T* vs = static_cast<T*>(p.v_slots) + (size_t)unit * k * D;
-  for (int idx = tid; idx < n_keep * CPR; idx += kThreads) {
-    const int s = idx / CPR, ch = idx - s * CPR;
-    const size_t src = (size_t)slot_of[s] * D + ch * VEC, dst = (size_t)s * D + ch * VEC;
-    st16(ks + dst, ld16(K + src));
-    st16(vs + dst, ld16(V + src));
+  const int total = n_keep * CPR;
+  for (int base = 0; base < total; base += B * kThreads) {
+    uint4 kr[B], vr[B];
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      const int idx = base + i * kThreads + tid;
+      const int s = idx < total ? idx / CPR : 0, ch = idx < total ? idx - s * CPR : 0;
+      const size_t src = (size_t)slot_of[s] * D + ch * VEC;
+      kr[i] = ld16(K + src);
+      vr[i] = ld16(V + src);
+    }
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      const int idx = base + i * kThreads + tid;
+      if (idx < total) {
+        const int s = idx / CPR, ch = idx - s * CPR;
+        const size_t dst = (size_t)s * D + ch * VEC;
+        st16(ks + dst, kr[i]);
+        st16(vs + dst, vr[i]);
+      }
+    }
   }
 }
 
@@ -132,7 +198,8 @@ __global__ void reset_kernel(ResetParams p) {
 
 template <typename T, int D>
 hipError_t seed(const SeedParams& p, hipStream_t s) {
-  const size_t lds = (size_t)(p.k_heavy + p.k_local) * sizeof(int);
+  const int k = p.k_heavy + p.k_local;
+  const size_t lds = (size_t)k * sizeof(int) + (stage_bits(p.T, k) ? (size_t)p.T * 4 : 0);
   seed_kernel<T, D><<<dim3((unsigned)p.units), dim3(kThreads), lds, s>>>(p);
   return hipGetLastError();
 }

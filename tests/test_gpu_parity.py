@@ -212,3 +212,33 @@ def test_stream_bf16_fill_then_evict_sampled_heads():
     agg = check_units(w, x, r, [0, 9, 22, 31])
     announce(f"[parity] {w.name}: decode {agg['decode_out']:.2e} acc {agg['acc_rel']:.2e} "
              f"ties={len(agg['ties'])}")
+
+
+def test_prefill_exact_ties_keep_the_newest():
+    # Dead keys point against every query, so their column sums underflow to exactly 0
+    # on both sides; k_heavy exceeds the live candidates, so the heavy cutoff falls
+    # among exact ties and the newest dead positions must be the ones kept.
+    w = Workload(98, "ties-f16", 1, 1, 2, 128, "f16", 64, 8, 20, 4)
+    announce(f"[parity] {w.name}: exact zero column sums at the heavy cutoff")
+    g = torch.Generator(device="cpu").manual_seed(98)
+    N = w.prompt + w.steps
+    qrow = torch.full((w.head_dim,), 0.5)
+    Q = qrow.expand(N, w.batch, w.heads, w.head_dim).clone()
+    K = torch.randn(N, w.batch, w.heads, w.head_dim, generator=g) * 0.5
+    V = torch.randn(N, w.batch, w.heads, w.head_dim, generator=g)
+    live = {0, 3, 7, 12, 20, 21, 33, 40, 47, 55}          # all other prompt candidates die
+    for j in range(w.prompt - w.k_local):
+        if j not in live:
+            K[j] = -100.0 * qrow
+    x = {}
+    for name, full in (("q", Q), ("k", K), ("v", V)):
+        full = full.to(w.torch_dtype).cuda()
+        x[f"{name}_prompt"] = full[:w.prompt].permute(1, 2, 0, 3).contiguous()
+        x[f"{name}_dec"] = full[w.prompt:].contiguous()
+    r = run_gpu(w, x)
+    cs = r["colsum"][0, 0].cpu()
+    dead = [j for j in range(w.prompt - w.k_local) if j not in live]
+    assert bool((cs[dead] == 0).all())
+    kept = sorted(int(p) for p in r["pos0"][0, 0].cpu() if p >= 0)
+    assert kept == sorted(sorted(live) + dead[-10:] + list(range(w.prompt - w.k_local, w.prompt)))
+    check_units(w, x, r, range(w.units_per_layer))
