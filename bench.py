@@ -18,7 +18,9 @@ Timing:
     decode phase divided by its 32 launches is the decode kernel's mean device
     duration used for the roofline (it agrees with rocprofv3's kernel trace);
   * graph replays are checked bit for bit against an eager run;
-  * cpu_baseline: the CPU oracle on the same inputs (all 256 units of one step).
+  * cpu_baseline: the CPU oracle on the same inputs (all 256 units of one step);
+  * prefill_mfma_opt30b: the prefill of the OPT-30B-shaped layer (T = 2048), where
+    prefill is MFMA-bound, against the 2.5 PFLOP/s dense fp16 peak.
 """
 from __future__ import annotations
 
@@ -34,6 +36,31 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published
 METRIC = "H2O decode tokens/s at 20% KV budget + % of HBM roofline (prefill % MFMA peak)"
+
+# HBM bytes per decode launch on this workload from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
+# runs of this script, scaled by the same counters on a plain 512 MiB copy
+# (`--copy-probe`). They describe one build of the decode kernel: the hash of its sources
+# is recorded with them, and the figure is reported only while the sources still match.
+DECODE_SOURCES = ("kv_cache_eviction_03_amd/csrc/decode.hip",
+                  "kv_cache_eviction_03_amd/csrc/h2o_device.hpp")
+DECODE_TRAFFIC = {"sha256": "28b2e6bf6590326ae489984d2a3bffd860cc43eec95abed3b79eef588e82edcf",
+                  "read_bytes": 14180754, "write_bytes": 376832}
+
+
+def decode_sources_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in DECODE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def decode_traffic():
+    t = DECODE_TRAFFIC
+    if t["sha256"] is None or t["sha256"] != decode_sources_hash():
+        return None
+    return t["read_bytes"] + t["write_bytes"]
 
 
 def decode_bytes_per_unit(w) -> int:
@@ -51,6 +78,43 @@ def prefill_flops_per_unit(w) -> int:
 def prefill_bytes_per_unit(w) -> int:
     T, d, s, k = w.prompt, w.head_dim, w.elem_bytes, w.k
     return 3 * T * d * s + 4 * T * d + 4 * T + 2 * k * d * s + 8 * k
+
+
+def prefill_mfma_probe(reps=3):
+    """Prefill of the OPT-30B-shaped layer (T = 2048, MFMA-bound) timed with HIP events."""
+    import torch
+
+    from kv_cache_eviction_03_amd import H2OCache
+    from workloads import WORKLOADS, generate
+    w = WORKLOADS[4].scaled(steps=0)
+    x = generate(w, seed=0, device="cuda:0")
+    c = H2OCache(w.batch, w.heads, w.head_dim, w.k_heavy, w.k_local, w.torch_dtype, "cuda:0",
+                 max_prompt=w.prompt)
+    out = torch.empty((w.batch, w.heads, w.prompt, w.head_dim), dtype=torch.float32, device="cuda:0")
+    cs = torch.empty((w.batch, w.heads, w.prompt), dtype=torch.float32, device="cuda:0")
+    c.prefill(x["q_prompt"], x["k_prompt"], x["v_prompt"], out=out, colsum=cs)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        c.prefill(x["q_prompt"], x["k_prompt"], x["v_prompt"], out=out, colsum=cs)
+    b.record()
+    torch.cuda.synchronize()
+    us = 1e3 * a.elapsed_time(b) / reps
+    flops = prefill_flops_per_unit(w) * w.units_per_layer
+    tflops = flops / (us * 1e-6) / 1e12
+    res = {"workload": f"{w.name}: batch {w.batch}, {w.heads} heads, d {w.head_dim}, fp16, "
+                       f"prompt {w.prompt}, k = {w.k_heavy}+{w.k_local}",
+           "bound": "mfma (arithmetic intensity %.0f flop/B > ridge 312.5)" % (
+               prefill_flops_per_unit(w) / prefill_bytes_per_unit(w)),
+           "prefill_us": us, "achieved_tflops": tflops, "peak_tflops": MFMA_F16_PEAK_TFLOPS,
+           "frac": tflops / MFMA_F16_PEAK_TFLOPS,
+           "prompt_tokens_per_s": w.batch * w.prompt / (us * 1e-6),
+           "note": "algorithmic flops 2T(T+1)d per unit over one h2o_prefill call "
+                   "(attention + column sums + seeding)"}
+    del x, c, out, cs
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(w, x, units):
@@ -82,6 +146,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mfma-probe", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 512 MiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the H2O path has no cross-GPU exchange and this "
@@ -89,6 +156,16 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_probe:
+        n = 512 << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 3}))
+        return
 
     from kv_cache_eviction_03_amd import H2OCache
     from workloads import WORKLOADS, generate
@@ -202,9 +279,10 @@ def main():
         "prefill_tokens_per_s": B * T / (pre_ms * 1e-3),
         "phase_ms": {"prefill": pre_ms, "decode": dec_ms},
         "roofline": {
-            "bound": "hbm", "kernel": "decode_kernel<_Float16,128> (one launch per decode step)",
+            "bound": "hbm",
+            "kernel": "decode_resident_kernel<_Float16,128,8> (one launch per decode step)",
             "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": dec_gbs / HBM_PEAK_GBS, "traffic": None,
+            "frac": dec_gbs / HBM_PEAK_GBS, "traffic": decode_traffic(),
             "avg_launch_us": dec_kernel_us, "algorithmic_bytes_per_launch": dec_bytes,
             "duration_from": "HIP events around the graph-replayed decode phase / launches",
         },
@@ -219,6 +297,8 @@ def main():
         },
         "wall_s_timed_loop": wall,
     }
+    if not args.no_mfma_probe:
+        result["prefill_mfma_opt30b"] = prefill_mfma_probe()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, x, list(range(units)))
     print(json.dumps(result), flush=True)

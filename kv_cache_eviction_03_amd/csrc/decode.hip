@@ -115,7 +115,7 @@ __device__ __forceinline__ void group_softmax(const uint4& qr, float qk_scale, c
   for (int i = 0; i < VEC; ++i) o[i] = 0.f;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    const float e = exp2f(s[u] - mref);
+    const float e = fast_exp2(s[u] - mref);
     lg += e;
     float vf[VEC];
     unpack(vr[u], vf, T{});
@@ -137,7 +137,7 @@ __global__ __launch_bounds__(kThreads) void decode_resident_kernel(DecodeParams 
   __shared__ __attribute__((aligned(16))) float s_red[ROWS * D];
   __shared__ float s_m[ROWS], s_l[ROWS];
   __shared__ float s_logit[ROWS * U];
-  __shared__ unsigned long long s_best;
+  __shared__ uint64_t s_key[kWaves];
 
   const int unit = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -163,7 +163,6 @@ __global__ __launch_bounds__(kThreads) void decode_resident_kernel(DecodeParams 
   const int jc = own ? jo : 0;
   const float acc_old = acc[jc];
   const int pos_old = pos[jc];
-  if (tid == 0) s_best = ~0ull;
   __builtin_amdgcn_sched_barrier(0);            // keep every load ahead of the math
 
   float s[U], mg, lg, o[VEC];
@@ -186,11 +185,11 @@ __global__ __launch_bounds__(kThreads) void decode_resident_kernel(DecodeParams 
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
     const float mr = s_m[r];
-    sc[r] = mr == -INFINITY ? 0.f : exp2f(mr - M);
+    sc[r] = mr == -INFINITY ? 0.f : fast_exp2(mr - M);
     L = fmaf(s_l[r], sc[r], L);
   }
   const float inv = 1.0f / L;
-  const float p_new = exp2f(s_logit[n] - M) * inv;
+  const float p_new = fast_exp2(s_logit[n] - M) * inv;
 
   for (int c = tid; c < D; c += kThreads) {
     float v = 0.f;
@@ -202,15 +201,16 @@ __global__ __launch_bounds__(kThreads) void decode_resident_kernel(DecodeParams 
   uint64_t key = ~0ull;
   float a = 0.f;
   if (own) {
-    a = acc_old + exp2f(s_logit[jo] - M) * inv;
+    a = acc_old + fast_exp2(s_logit[jo] - M) * inv;
     acc[jo] = a;
-    if (full && pos_old <= limit) {
-      key = score_key(a, pos_old);
-      atomicMin(&s_best, (unsigned long long)key);   // order-independent minimum
-    }
+    if (full && pos_old <= limit) key = score_key(a, pos_old);
   }
+  const uint64_t wmin = wave_min_u64(key);
+  if (lane == 0) s_key[wave] = wmin;
   __syncthreads();                              // (2)
-  const uint64_t best = s_best;
+  uint64_t best = s_key[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) best = s_key[w] < best ? s_key[w] : best;
 
   int dst = -1;
   bool meta = false;
@@ -245,7 +245,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p, 
   constexpr int C = ROWS * U;                   // slots per workgroup
   __shared__ __attribute__((aligned(16))) float s_red[ROWS * D];
   __shared__ float s_m[ROWS], s_l[ROWS];
-  __shared__ unsigned long long s_best;
+  __shared__ uint64_t s_key[kWaves];
   __shared__ int s_last, s_dst;
 
   const int nsplit = w.splits;
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p, 
   float sc[ROWS], l = 0.f;
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
-    sc[r] = s_m[r] == -INFINITY ? 0.f : exp2f(s_m[r] - m);
+    sc[r] = s_m[r] == -INFINITY ? 0.f : fast_exp2(s_m[r] - m);
     l = fmaf(s_l[r], sc[r], l);
   }
   for (int c = tid; c < D; c += kThreads) {
@@ -319,7 +319,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p, 
   float L = 0.f;
   for (int q = 0; q < nsplit; ++q) {
     const float mq = ml[2 * q];
-    if (mq != -INFINITY) L = fmaf(ml[2 * q + 1], exp2f(mq - M), L);
+    if (mq != -INFINITY) L = fmaf(ml[2 * q + 1], fast_exp2(mq - M), L);
   }
   const float inv = 1.0f / L;
   for (int c = tid; c < D; c += kThreads) {
@@ -328,21 +328,17 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p, 
       const float mq = ml[2 * q];
       if (mq != -INFINITY)
         v = fmaf(w.part_o[((size_t)unit * nsplit + q) * D + c],
-                 exp2f(mq - M), v);
+                 fast_exp2(mq - M), v);
     }
     p.out[(size_t)unit * D + c] = v * inv;
   }
-  const float p_new = exp2f(logit[n] - M) * inv;
-  if (tid == 0) {
-    s_best = ~0ull;
-    s_dst = full ? -1 : n;
-  }
-  __syncthreads();
+  const float p_new = fast_exp2(logit[n] - M) * inv;
+  if (tid == 0) s_dst = full ? -1 : n;
 
   uint64_t best = ~0ull;
   int best_slot = -1;
   for (int j = tid; j < n; j += kThreads) {
-    const float a = acc[j] + exp2f(logit[j] - M) * inv;
+    const float a = acc[j] + fast_exp2(logit[j] - M) * inv;
     acc[j] = a;
     const int ps = pos[j];
     if (full && ps <= limit) {
@@ -350,9 +346,12 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p, 
       if (key < best) { best = key; best_slot = j; }
     }
   }
-  if (best_slot >= 0) atomicMin(&s_best, (unsigned long long)best);
+  const uint64_t wmin = wave_min_u64(best);
+  if (lane == 0) s_key[wave] = wmin;
   __syncthreads();
-  const uint64_t gbest = s_best;
+  uint64_t gbest = s_key[0];
+#pragma unroll
+  for (int q = 1; q < kWaves; ++q) gbest = s_key[q] < gbest ? s_key[q] : gbest;
   const bool mine = full && best_slot >= 0 && best == gbest;
   if (mine) s_dst = best_slot;
   __syncthreads();

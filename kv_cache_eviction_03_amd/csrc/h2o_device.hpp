@@ -8,6 +8,12 @@
 namespace h2o {
 
 constexpr float kLog2e = 1.4426950408889634f;
+
+// 2^x with the bare v_exp_f32 (about 1 ulp). The library exp2f wraps it in a
+// rescale so that results below 2^-126 come out as denormals; softmax weights
+// that small are irrelevant (they flush to 0 here), and the wrapper costs five
+// extra VALU instructions per call.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 constexpr int kWave = 64;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -68,12 +74,23 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
   const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, kWave);
   return ((uint64_t)hi << 32) | lo;
 }
+// DPP lane move of a 64-bit value inside 16-lane rows (all lanes active).
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xf, 0xf, false);
+  const uint32_t hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xf, 0xf, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+// Minimum over the wave, every lane gets it: four DPP steps inside each 16-lane row
+// (symmetric pairings), then two shuffles across rows.
 __device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint64_t w = shfl_xor_u64(v, o);
-    v = w < v ? w : v;
-  }
+  uint64_t w;
+  w = dpp_u64<0xb1>(v); v = w < v ? w : v;     // quad_perm [1,0,3,2]
+  w = dpp_u64<0x4e>(v); v = w < v ? w : v;     // quad_perm [2,3,0,1]
+  w = dpp_u64<0x141>(v); v = w < v ? w : v;    // row_half_mirror
+  w = dpp_u64<0x140>(v); v = w < v ? w : v;    // row_mirror
+  w = shfl_xor_u64(v, 16); v = w < v ? w : v;
+  w = shfl_xor_u64(v, 32); v = w < v ? w : v;
   return v;
 }
 

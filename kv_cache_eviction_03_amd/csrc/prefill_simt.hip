@@ -66,8 +66,8 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(PrefillParams p) {
     float s = dot16<D>(qv, kv) * p.qk_scale;
     if (j > qc) s = -INFINITY;
     const float mn = fmaxf(m, s);
-    const float alpha = exp2f(m - mn);
-    const float pj = exp2f(s - mn);
+    const float alpha = fast_exp2(m - mn);
+    const float pj = fast_exp2(s - mn);
     l = l * alpha + pj;
 #pragma unroll
     for (int i = 0; i < DP; ++i) o[i] = fmaf(pj, vv[i], o[i] * alpha);
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(kThreads) void colsum_f32_kernel(PrefillParams p) {
     float qv[DP];
     load_part<D>(Q + (size_t)i * D, part, qv);
     const float s = dot16<D>(qv, kv) * p.qk_scale;
-    if (i >= kj) cs += exp2f(s - lse[i]);
+    if (i >= kj) cs += fast_exp2(s - lse[i]);
   }
   if (part == 0 && kj < T_) p.colsum[(size_t)unit * T_ + kj] = cs;
 }
