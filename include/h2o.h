@@ -20,8 +20,7 @@
  * Memory. Every pointer passed to these functions is DEVICE memory owned by the
  * caller (except the descriptor and aux structs themselves, which are host
  * structs read during the call only). The library never allocates, frees or
- * synchronises, keeps no pointer after a call returns, and holds no state
- * besides a per-process cache of device properties.
+ * synchronises, keeps no pointer after a call returns, and holds no state.
  *
  * Streams. `stream` is a hipStream_t passed as void* (NULL = the null stream).
  * Every call enqueues its kernels on that stream and returns without waiting.
@@ -119,12 +118,11 @@ h2o_status h2o_reset(const h2o_cache_desc* cache, void* stream);
  * up to max_prompt tokens and by h2o_decode_step on this descriptor's shape.
  * Returns 0 for an invalid descriptor or max_prompt < 0.
  *
- * Workspace contract: 256-byte aligned device memory, owned by the caller,
- * ZERO-FILLED ONCE before its first use. Its leading bytes hold per-unit arrival
- * counters of the decode step when the decode splits a unit's slots over
- * several workgroups (large k or few units); every call leaves them zero again.
- * The rest is scratch whose contents on entry are ignored. One workspace must
- * not be used by two calls that can run at the same time.
+ * Workspace contract: 256-byte aligned device memory owned by the caller. It is
+ * scratch: its contents on entry are ignored and on return are unspecified
+ * (prefill keeps row log-sum-exps there; a decode that spreads a unit's slots
+ * over several workgroups keeps per-workgroup partials there). One workspace
+ * must not be used by two calls that can run at the same time.
  */
 size_t h2o_workspace_bytes(const h2o_cache_desc* cache, int32_t max_prompt);
 

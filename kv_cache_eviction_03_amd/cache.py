@@ -45,7 +45,7 @@ class H2OCache:
         self.acc_score = torch.zeros((batch, heads, self.k), dtype=torch.float32,
                                      device=self.device)
         self.t = 0
-        self.workspace = torch.zeros(0, dtype=torch.uint8, device=self.device)
+        self.workspace = torch.empty(0, dtype=torch.uint8, device=self.device)
         self.reserve(max_prompt)
 
     def desc(self) -> CacheDesc:
@@ -57,8 +57,7 @@ class H2OCache:
     def reserve(self, max_prompt: int) -> None:
         need = h2o_workspace_bytes(self.desc(), max_prompt)
         if need > self.workspace.numel():
-            # zero-filled: the leading decode counters must start at zero
-            self.workspace = torch.zeros(need, dtype=torch.uint8, device=self.device)
+            self.workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
 
     def _check(self, x: torch.Tensor, shape, name: str) -> None:
         if x.dtype != self.dtype or tuple(x.shape) != tuple(shape) or not x.is_contiguous() \

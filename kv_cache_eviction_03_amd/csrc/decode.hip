@@ -14,7 +14,7 @@
 //      slot n.
 //
 // Memory plan. A slot row is D*sizeof(T) bytes, read as 16-byte chunks by LANES
-// consecutive lanes (a "row group"); a 256-thread workgroup has ROWS row
+// consecutive lanes (a "row group"); a workgroup of THREADS threads has ROWS row
 // groups and covers ROWS slots per pass, every wave load fully coalesced.
 // Row group g owns slots j = u*ROWS + g, u < U, and issues all of their K and
 // V loads (plus q, the scores and the positions) before consuming any, so the
@@ -22,15 +22,18 @@
 // new token's row (always valid memory) and masked, so the load stream has no
 // branches. Logit sums over a row group use DPP lane moves.
 //
-// Two kernels:
-//   * resident: one workgroup per unit when k + 1 <= ROWS * U (U = 8 or 16):
-//     two barriers, everything else in registers.
-//   * split: S workgroups per unit, one slot chunk each, for large k or few
-//     units. Each writes (max, sum, unnormalised out) and its logits to the
-//     workspace, then bumps a per-unit counter with agent-scope acq_rel
-//     ordering; the last arrival combines the partials, updates the scores,
-//     takes the argmin and overwrites the victim (every other workgroup has
-//     finished reading it), then puts the counter back to zero.
+// Kernels:
+//   * resident: one workgroup per unit (256 or 1024 threads) when the unit fits
+//     one load batch (k + 1 <= ROWS * 8). Row groups publish (max, sum,
+//     unnormalised out) in LDS; wave 0 turns them into scale factors; owners
+//     update their scores and the (acc, pos) minimum is a wave minimum plus an
+//     LDS stage. Three barriers, no global scratch.
+//   * split: for larger k, two launches. split_partial gives S workgroups per
+//     unit one slot chunk each and writes (max, sum, unnormalised out) plus the
+//     chunk's logits to the workspace; split_combine (one 1024-thread workgroup
+//     per unit) merges the partials, updates every score, takes the argmin and
+//     overwrites the victim. The kernel boundary orders the two, so no
+//     workgroup ever waits on another and no device-scope fence is needed.
 // The victim is chosen with 64-bit keys (fp32 score bits << 32 | position):
 // scores are >= 0, so the integer order is the (score, position) order.
 // All reductions run in a fixed order: results are bit-reproducible.
@@ -40,14 +43,13 @@
 namespace h2o {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
+constexpr int kBatch = 8;         // slot rows per row group in one load batch
 
-template <typename T, int D> struct Shape {
+template <typename T, int D, int THREADS = 256> struct Shape {
   static constexpr int VEC = Chunk<T>::N;       // elements per 16-byte chunk
   static constexpr int LANES = D / VEC;         // lanes per slot row
-  static constexpr int ROWS = kThreads / LANES; // row groups per workgroup
-  static constexpr int GPW = kWave / LANES;     // row groups per wave
+  static constexpr int ROWS = THREADS / LANES;  // row groups per workgroup
+  static constexpr int WAVES = THREADS / kWave;
 };
 
 // DPP lane move inside a 16-lane row (all lanes active).
@@ -69,11 +71,11 @@ __device__ __forceinline__ float row_sum(float v) {
 }
 
 // Loads of one row group: K and V chunks of its U slots (clamped to the new token row).
-template <typename T, int D, int U>
+template <typename T, int D, int U, int THREADS>
 __device__ __forceinline__ void load_rows(const T* ks, const T* vs, const T* kn, const T* vn,
                                           int first, int n, int rl, uint4 (&kr)[U],
                                           uint4 (&vr)[U]) {
-  using S = Shape<T, D>;
+  using S = Shape<T, D, THREADS>;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int j = first + u * S::ROWS;
@@ -86,12 +88,12 @@ __device__ __forceinline__ void load_rows(const T* ks, const T* vs, const T* kn,
 
 // Logits (log2 domain) of a row group's U slots; slots past `last` are -inf.
 // Returns the group max, its sum of 2^(s - max) and the unnormalised out chunk.
-template <typename T, int D, int U>
+template <typename T, int D, int U, int THREADS>
 __device__ __forceinline__ void group_softmax(const uint4& qr, float qk_scale, const uint4 (&kr)[U],
                                               const uint4 (&vr)[U], int first, int last,
                                               float (&s)[U], float& mg, float& lg,
                                               float (&o)[Shape<T, D>::VEC]) {
-  using S = Shape<T, D>;
+  using S = Shape<T, D, THREADS>;
   constexpr int VEC = S::VEC;
   float qf[VEC];
   unpack(qr, qf, T{});
@@ -128,16 +130,41 @@ __device__ __forceinline__ uint64_t score_key(float a, int pos) {
   return ((uint64_t)__float_as_uint(a) << 32) | (uint32_t)pos;
 }
 
+
+// Row-group partials in LDS -> per-group scale factors 2^(m_g - M), the global max M
+// and 1 / sum, computed once by wave 0 (fixed order) and published in LDS.
+template <int ROWS>
+__device__ __forceinline__ void combine_groups(const float* s_m, const float* s_l, float* s_sc,
+                                               float* s_stat, int tid) {
+  static_assert(ROWS <= 2 * kWave, "at most two row groups per lane of wave 0");
+  if (tid < kWave) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int r = tid; r < ROWS; r += kWave) m = fmaxf(m, s_m[r]);
+    m = group_max<kWave>(m);
+    float l = 0.f;
+#pragma unroll
+    for (int r = tid; r < ROWS; r += kWave) {
+      const float sc = s_m[r] == -INFINITY ? 0.f : fast_exp2(s_m[r] - m);
+      s_sc[r] = sc;
+      l = fmaf(s_l[r], sc, l);
+    }
+    l = group_sum<kWave>(l);
+    if (tid == 0) { s_stat[0] = m; s_stat[1] = 1.0f / l; }
+  }
+}
+
 // ------------------------------------------------------------------ resident --
 
-template <typename T, int D, int U>
-__global__ __launch_bounds__(kThreads) void decode_resident_kernel(DecodeParams p) {
-  using S = Shape<T, D>;
-  constexpr int VEC = S::VEC, LANES = S::LANES, ROWS = S::ROWS;
+template <typename T, int D, int THREADS>
+__global__ __launch_bounds__(THREADS) void decode_resident_kernel(DecodeParams p) {
+  using S = Shape<T, D, THREADS>;
+  constexpr int VEC = S::VEC, LANES = S::LANES, ROWS = S::ROWS, U = kBatch;
+  static_assert(U <= LANES, "a lane owns one slot score");
   __shared__ __attribute__((aligned(16))) float s_red[ROWS * D];
-  __shared__ float s_m[ROWS], s_l[ROWS];
+  __shared__ float s_m[ROWS], s_l[ROWS], s_sc[ROWS], s_stat[2];
   __shared__ float s_logit[ROWS * U];
-  __shared__ uint64_t s_key[kWaves];
+  __shared__ uint64_t s_key[S::WAVES];
 
   const int unit = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -157,16 +184,17 @@ __global__ __launch_bounds__(kThreads) void decode_resident_kernel(DecodeParams 
   // Every load of the unit, issued before any is consumed.
   const uint4 qr = ld16(static_cast<const T*>(p.q) + (size_t)unit * D + rl * VEC);
   uint4 kr[U], vr[U];
-  load_rows<T, D, U>(ks, vs, kn, vn, g, n, rl, kr, vr);
+  load_rows<T, D, U, THREADS>(ks, vs, kn, vn, g, n, rl, kr, vr);
   const int jo = rl * ROWS + g;                 // slot whose score this lane owns
   const bool own = rl < U && jo < n;
   const int jc = own ? jo : 0;
   const float acc_old = acc[jc];
   const int pos_old = pos[jc];
+  const uint4 knr = ld16(kn + rl * VEC), vnr = ld16(vn + rl * VEC);
   __builtin_amdgcn_sched_barrier(0);            // keep every load ahead of the math
 
   float s[U], mg, lg, o[VEC];
-  group_softmax<T, D, U>(qr, p.qk_scale, kr, vr, g, n, s, mg, lg, o);
+  group_softmax<T, D, U, THREADS>(qr, p.qk_scale, kr, vr, g, n, s, mg, lg, o);
 
 #pragma unroll
   for (int i = 0; i < VEC; ++i) s_red[g * D + rl * VEC + i] = o[i];
@@ -177,24 +205,38 @@ __global__ __launch_bounds__(kThreads) void decode_resident_kernel(DecodeParams 
     for (int u = 0; u < U; ++u) s_logit[u * ROWS + g] = s[u];
   }
   __syncthreads();                              // (1) every K/V read is consumed
-
-  float M = -INFINITY;
+  // Scale factors 2^(m_g - M) of the row groups. With few groups every thread forms
+  // them itself in registers (no extra barrier); with many, wave 0 forms them once.
+  float M, inv;
+  float sc[ROWS <= 16 ? ROWS : 1];
+  if constexpr (ROWS <= 16) {
+    M = -INFINITY;
 #pragma unroll
-  for (int r = 0; r < ROWS; ++r) M = fmaxf(M, s_m[r]);
-  float sc[ROWS], L = 0.f;
+    for (int r = 0; r < ROWS; ++r) M = fmaxf(M, s_m[r]);
+    float L = 0.f;
 #pragma unroll
-  for (int r = 0; r < ROWS; ++r) {
-    const float mr = s_m[r];
-    sc[r] = mr == -INFINITY ? 0.f : fast_exp2(mr - M);
-    L = fmaf(s_l[r], sc[r], L);
+    for (int r = 0; r < ROWS; ++r) {
+      sc[r] = s_m[r] == -INFINITY ? 0.f : fast_exp2(s_m[r] - M);
+      L = fmaf(s_l[r], sc[r], L);
+    }
+    inv = 1.0f / L;
+  } else {
+    combine_groups<ROWS>(s_m, s_l, s_sc, s_stat, tid);
+    __syncthreads();                            // (2)
+    M = s_stat[0];
+    inv = s_stat[1];
   }
-  const float inv = 1.0f / L;
   const float p_new = fast_exp2(s_logit[n] - M) * inv;
 
-  for (int c = tid; c < D; c += kThreads) {
+  for (int c = tid; c < D; c += THREADS) {
     float v = 0.f;
+    if constexpr (ROWS <= 16) {
 #pragma unroll
-    for (int r = 0; r < ROWS; ++r) v = fmaf(s_red[r * D + c], sc[r], v);
+      for (int r = 0; r < ROWS; ++r) v = fmaf(s_red[r * D + c], sc[r], v);
+    } else {
+#pragma unroll 8
+      for (int r = 0; r < ROWS; ++r) v = fmaf(s_red[r * D + c], s_sc[r], v);
+    }
     p.out[(size_t)unit * D + c] = v * inv;
   }
 
@@ -207,10 +249,10 @@ __global__ __launch_bounds__(kThreads) void decode_resident_kernel(DecodeParams 
   }
   const uint64_t wmin = wave_min_u64(key);
   if (lane == 0) s_key[wave] = wmin;
-  __syncthreads();                              // (2)
+  __syncthreads();                              // (3)
   uint64_t best = s_key[0];
 #pragma unroll
-  for (int w = 1; w < kWaves; ++w) best = s_key[w] < best ? s_key[w] : best;
+  for (int w = 1; w < S::WAVES; ++w) best = s_key[w] < best ? s_key[w] : best;
 
   int dst = -1;
   bool meta = false;
@@ -224,8 +266,8 @@ __global__ __launch_bounds__(kThreads) void decode_resident_kernel(DecodeParams 
     meta = jo == n;
   }
   if (dst >= 0) {
-    st16(ks + (size_t)dst * D + rl * VEC, ld16(kn + rl * VEC));
-    st16(vs + (size_t)dst * D + rl * VEC, ld16(vn + rl * VEC));
+    st16(ks + (size_t)dst * D + rl * VEC, knr);
+    st16(vs + (size_t)dst * D + rl * VEC, vnr);
   }
   if (meta) {                                   // the lane that wrote acc[dst] above, if any
     pos[dst] = t;
@@ -238,43 +280,37 @@ __global__ __launch_bounds__(kThreads) void decode_resident_kernel(DecodeParams 
 
 // --------------------------------------------------------------------- split --
 
-template <typename T, int D, int U>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p, SplitScratch w) {
-  using S = Shape<T, D>;
-  constexpr int VEC = S::VEC, LANES = S::LANES, ROWS = S::ROWS;
+constexpr int kPartThreads = 256;
+constexpr int kCombThreads = 1024;
+
+template <typename T, int D>
+__global__ __launch_bounds__(kPartThreads) void decode_split_partial_kernel(DecodeParams p,
+                                                                            SplitScratch w) {
+  using S = Shape<T, D, kPartThreads>;
+  constexpr int VEC = S::VEC, LANES = S::LANES, ROWS = S::ROWS, U = kBatch;
   constexpr int C = ROWS * U;                   // slots per workgroup
   __shared__ __attribute__((aligned(16))) float s_red[ROWS * D];
-  __shared__ float s_m[ROWS], s_l[ROWS];
-  __shared__ uint64_t s_key[kWaves];
-  __shared__ int s_last, s_dst;
+  __shared__ float s_m[ROWS], s_l[ROWS], s_sc[ROWS];
 
   const int nsplit = w.splits;
   const int unit = blockIdx.x / nsplit, sp = blockIdx.x - unit * nsplit;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int rl = tid % LANES, g = tid / LANES;
-  const int k = p.k, t = p.t;
-  const int n = min(k, t);
-  const bool full = n == k;
-  const int limit = t - p.k_local;
-
-  T* ks = static_cast<T*>(p.k_slots) + (size_t)unit * k * D;
-  T* vs = static_cast<T*>(p.v_slots) + (size_t)unit * k * D;
+  const int k = p.k, n = min(k, p.t);
+  const T* ks = static_cast<const T*>(p.k_slots) + (size_t)unit * k * D;
+  const T* vs = static_cast<const T*>(p.v_slots) + (size_t)unit * k * D;
   const T* kn = static_cast<const T*>(p.k_new) + (size_t)unit * D;
   const T* vn = static_cast<const T*>(p.v_new) + (size_t)unit * D;
-  int32_t* pos = p.slot_pos + (size_t)unit * k;
-  float* acc = p.acc + (size_t)unit * k;
   float* logit = w.logits + (size_t)unit * (k + 1);
-  float* pml = w.part_ml + ((size_t)unit * nsplit + sp) * 2;
-  float* po = w.part_o + ((size_t)unit * nsplit + sp) * D;
 
-  // Phase A: this workgroup's chunk [sp*C, sp*C + C) of the n + 1 keys.
+  // This workgroup's chunk [sp*C, sp*C + C) of the n + 1 keys.
   const int first = sp * C + g;
   const uint4 qr = ld16(static_cast<const T*>(p.q) + (size_t)unit * D + rl * VEC);
   uint4 kr[U], vr[U];
-  load_rows<T, D, U>(ks, vs, kn, vn, first, n, rl, kr, vr);
+  load_rows<T, D, U, kPartThreads>(ks, vs, kn, vn, first, n, rl, kr, vr);
   __builtin_amdgcn_sched_barrier(0);            // keep every load ahead of the math
   float s[U], mg, lg, o[VEC];
-  group_softmax<T, D, U>(qr, p.qk_scale, kr, vr, first, n, s, mg, lg, o);
+  group_softmax<T, D, U, kPartThreads>(qr, p.qk_scale, kr, vr, first, n, s, mg, lg, o);
   if (rl == 0) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -284,87 +320,137 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p, 
   for (int i = 0; i < VEC; ++i) s_red[g * D + rl * VEC + i] = o[i];
   if (rl == 0) { s_m[g] = mg; s_l[g] = lg; }
   __syncthreads();
-  float m = -INFINITY;
+  // Chunk partial: max m, sum l and out relative to m (1 / l is not applied).
+  if (tid < kWave) {
+    float m = -INFINITY;
 #pragma unroll
-  for (int r = 0; r < ROWS; ++r) m = fmaxf(m, s_m[r]);
-  float sc[ROWS], l = 0.f;
+    for (int r = tid; r < ROWS; r += kWave) m = fmaxf(m, s_m[r]);
+    m = group_max<kWave>(m);
+    float l = 0.f;
 #pragma unroll
-  for (int r = 0; r < ROWS; ++r) {
-    sc[r] = s_m[r] == -INFINITY ? 0.f : fast_exp2(s_m[r] - m);
-    l = fmaf(s_l[r], sc[r], l);
+    for (int r = tid; r < ROWS; r += kWave) {
+      const float sc = s_m[r] == -INFINITY ? 0.f : fast_exp2(s_m[r] - m);
+      s_sc[r] = sc;
+      l = fmaf(s_l[r], sc, l);
+    }
+    l = group_sum<kWave>(l);
+    if (tid == 0) {
+      float* pml = w.part_ml + ((size_t)unit * nsplit + sp) * 2;
+      pml[0] = m;
+      pml[1] = l;
+    }
   }
-  for (int c = tid; c < D; c += kThreads) {
+  __syncthreads();
+  float* po = w.part_o + ((size_t)unit * nsplit + sp) * D;
+  for (int c = tid; c < D; c += kPartThreads) {
     float v = 0.f;
 #pragma unroll
-    for (int r = 0; r < ROWS; ++r) v = fmaf(s_red[r * D + c], sc[r], v);
+    for (int r = 0; r < ROWS; ++r) v = fmaf(s_red[r * D + c], s_sc[r], v);
     po[c] = v;
   }
-  if (tid == 0) { pml[0] = m; pml[1] = l; }
+}
 
-  // Arrival: all of this workgroup's stores are ordered before the counter bump.
-  __syncthreads();
-  if (tid == 0) {
-    const int prev = __hip_atomic_fetch_add(w.counters + unit, 1, __ATOMIC_ACQ_REL,
-                                            __HIP_MEMORY_SCOPE_AGENT);
-    s_last = prev == nsplit - 1;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // other workgroups' partials are visible
+template <typename T, int D>
+__global__ __launch_bounds__(kCombThreads) void decode_split_combine_kernel(DecodeParams p,
+                                                                            SplitScratch w) {
+  constexpr int VEC = Chunk<T>::N, LANES = D / VEC;
+  constexpr int WAVES = kCombThreads / kWave;
+  constexpr int G = kCombThreads / D;           // groups that share the partial-out sums
+  constexpr int R = 4;                          // slots per thread per load batch
+  __shared__ float s_ml[2 * kMaxSplits], s_sc[kMaxSplits], s_stat[2];
+  __shared__ float s_o[G * D];
+  __shared__ uint64_t s_key[WAVES];
+  __shared__ int s_dst;
 
-  // Phase B (last arrival only): combine, score, choose, overwrite.
-  const float* ml = w.part_ml + (size_t)unit * nsplit * 2;
-  float M = -INFINITY;
-  for (int q = 0; q < nsplit; ++q) M = fmaxf(M, ml[2 * q]);
-  float L = 0.f;
-  for (int q = 0; q < nsplit; ++q) {
-    const float mq = ml[2 * q];
-    if (mq != -INFINITY) L = fmaf(ml[2 * q + 1], fast_exp2(mq - M), L);
-  }
-  const float inv = 1.0f / L;
-  for (int c = tid; c < D; c += kThreads) {
-    float v = 0.f;
-    for (int q = 0; q < nsplit; ++q) {
-      const float mq = ml[2 * q];
-      if (mq != -INFINITY)
-        v = fmaf(w.part_o[((size_t)unit * nsplit + q) * D + c],
-                 fast_exp2(mq - M), v);
-    }
-    p.out[(size_t)unit * D + c] = v * inv;
-  }
-  const float p_new = fast_exp2(logit[n] - M) * inv;
+  const int unit = blockIdx.x, nsplit = w.splits;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int k = p.k, t = p.t;
+  const int n = min(k, t);
+  const bool full = n == k;
+  const int limit = t - p.k_local;
+  T* ks = static_cast<T*>(p.k_slots) + (size_t)unit * k * D;
+  T* vs = static_cast<T*>(p.v_slots) + (size_t)unit * k * D;
+  const T* kn = static_cast<const T*>(p.k_new) + (size_t)unit * D;
+  const T* vn = static_cast<const T*>(p.v_new) + (size_t)unit * D;
+  int32_t* pos = p.slot_pos + (size_t)unit * k;
+  float* acc = p.acc + (size_t)unit * k;
+  const float* logit = w.logits + (size_t)unit * (k + 1);
+
+  if (tid < 2 * nsplit) s_ml[tid] = w.part_ml[(size_t)unit * nsplit * 2 + tid];
   if (tid == 0) s_dst = full ? -1 : n;
+  __syncthreads();
+  if (tid < kWave) {
+    float m = -INFINITY;
+    for (int q = tid; q < nsplit; q += kWave) m = fmaxf(m, s_ml[2 * q]);
+    m = group_max<kWave>(m);
+    float l = 0.f;
+    for (int q = tid; q < nsplit; q += kWave) {
+      const float sc = s_ml[2 * q] == -INFINITY ? 0.f : fast_exp2(s_ml[2 * q] - m);
+      s_sc[q] = sc;
+      l = fmaf(s_ml[2 * q + 1], sc, l);
+    }
+    l = group_sum<kWave>(l);
+    if (tid == 0) { s_stat[0] = m; s_stat[1] = 1.0f / l; }
+  }
+  __syncthreads();
+  const float M = s_stat[0], inv = s_stat[1];
 
+  // out: G groups of D threads each sum every G-th partial, then a fixed-order merge.
+  {
+    const int c = tid % D, grp = tid / D;
+    float v = 0.f;
+    for (int q = grp; q < nsplit; q += G)
+      v = fmaf(w.part_o[((size_t)unit * nsplit + q) * D + c], s_sc[q], v);
+    s_o[grp * D + c] = v;
+  }
+  // scores: slots j = tid + i * kCombThreads, R loads of each kind in flight
   uint64_t best = ~0ull;
   int best_slot = -1;
-  for (int j = tid; j < n; j += kThreads) {
-    const float a = acc[j] + fast_exp2(logit[j] - M) * inv;
-    acc[j] = a;
-    const int ps = pos[j];
-    if (full && ps <= limit) {
-      const uint64_t key = score_key(a, ps);
-      if (key < best) { best = key; best_slot = j; }
+  for (int base = 0; base < n; base += R * kCombThreads) {
+    float lg[R], ac[R];
+    int ps[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int j = base + i * kCombThreads + tid, jc = j < n ? j : 0;
+      lg[i] = logit[jc];
+      ac[i] = acc[jc];
+      ps[i] = pos[jc];
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int j = base + i * kCombThreads + tid;
+      if (j < n) {
+        const float a = ac[i] + fast_exp2(lg[i] - M) * inv;
+        acc[j] = a;
+        if (full && ps[i] <= limit) {
+          const uint64_t key = score_key(a, ps[i]);
+          if (key < best) { best = key; best_slot = j; }
+        }
+      }
     }
   }
   const uint64_t wmin = wave_min_u64(best);
   if (lane == 0) s_key[wave] = wmin;
   __syncthreads();
+  if (tid < D) {
+    float v = 0.f;
+#pragma unroll
+    for (int grp = 0; grp < G; ++grp) v += s_o[grp * D + tid];
+    p.out[(size_t)unit * D + tid] = v * inv;
+  }
   uint64_t gbest = s_key[0];
 #pragma unroll
-  for (int q = 1; q < kWaves; ++q) gbest = s_key[q] < gbest ? s_key[q] : gbest;
-  const bool mine = full && best_slot >= 0 && best == gbest;
-  if (mine) s_dst = best_slot;
+  for (int q = 1; q < WAVES; ++q) gbest = s_key[q] < gbest ? s_key[q] : gbest;
+  // The victim is the slot whose key is gbest (keys are unique: positions are); the thread
+  // that wrote its score publishes it and later writes its metadata, keeping them in order.
+  if (full && best_slot >= 0 && best == gbest) s_dst = best_slot;
   __syncthreads();
   const int dst = s_dst;
+  const float p_new = fast_exp2(logit[n] - M) * inv;
   if (dst >= 0) {
-    for (int c = tid; c < 2 * LANES; c += kThreads) {
-      const int ch = c % LANES;
-      T* row = (c < LANES ? ks : vs) + (size_t)dst * D + ch * VEC;
-      st16(row, ld16((c < LANES ? kn : vn) + ch * VEC));
-    }
-    // The metadata is written by the thread that updated acc[dst] in the loop above
-    // (j = dst is visited by thread dst % 256), so its two writes are in program order.
-    if (tid == (dst & (kThreads - 1))) {
+    if (tid < LANES) st16(ks + (size_t)dst * D + tid * VEC, ld16(kn + tid * VEC));
+    else if (tid < 2 * LANES) st16(vs + (size_t)dst * D + (tid - LANES) * VEC, ld16(vn + (tid - LANES) * VEC));
+    if (tid == dst % kCombThreads) {            // visited slot dst in the score loop
       pos[dst] = t;
       acc[dst] = p_new;
     }
@@ -374,7 +460,6 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p, 
     if (p.evicted_pos) p.evicted_pos[unit] = full && dst >= 0 ? (int32_t)(uint32_t)gbest : -1;
     if (p.evicted_acc)
       p.evicted_acc[unit] = full && dst >= 0 ? __uint_as_float((uint32_t)(gbest >> 32)) : 0.f;
-    w.counters[unit] = 0;                       // ready for the next step
   }
 }
 
@@ -384,54 +469,46 @@ template <typename T, int D>
 hipError_t run(const DecodeParams& p, const SplitScratch& w, hipStream_t s) {
   const DecodePlan plan = plan_decode(sizeof(T), D, p.k, p.units);
   if (plan.splits == 0) {
-    if constexpr (Shape<T, D>::LANES >= 16) {
-      if (plan.u == 16) {
-        decode_resident_kernel<T, D, 16><<<dim3(p.units), dim3(kThreads), 0, s>>>(p);
-        return hipGetLastError();
-      }
-    }
-    decode_resident_kernel<T, D, 8><<<dim3(p.units), dim3(kThreads), 0, s>>>(p);
-  } else {
-    decode_split_kernel<T, D, kSplitU><<<dim3((unsigned)(p.units * plan.splits)), dim3(kThreads),
-                                         0, s>>>(p, w);
+    if (plan.threads == 256)
+      decode_resident_kernel<T, D, 256><<<dim3(p.units), dim3(256), 0, s>>>(p);
+    else
+      decode_resident_kernel<T, D, 1024><<<dim3(p.units), dim3(1024), 0, s>>>(p);
+    return hipGetLastError();
   }
+  decode_split_partial_kernel<T, D>
+      <<<dim3((unsigned)(p.units * plan.splits)), dim3(kPartThreads), 0, s>>>(p, w);
+  if (hipError_t e = hipGetLastError()) return e;
+  decode_split_combine_kernel<T, D><<<dim3(p.units), dim3(kCombThreads), 0, s>>>(p, w);
   return hipGetLastError();
 }
 
 }  // namespace
 
 DecodePlan plan_decode(int elem_bytes, int D, int k, int units) {
-  const int rows = kThreads / (D * elem_bytes / 16);
-  DecodePlan plan{0, 0};
-  // One resident workgroup per unit while the whole cache fits one load batch and the
-  // units alone fill most of the chip; otherwise split the slots over workgroups.
-  const int lanes = kThreads / rows;             // a lane owns one slot score: u <= lanes
-  if (units >= 128 || k + 1 <= rows * 8) {
-    if (k + 1 <= rows * 8) { plan.u = 8; return plan; }
-    if (k + 1 <= rows * 16 && lanes >= 16) { plan.u = 16; return plan; }
-  }
-  plan.u = kSplitU;
-  plan.splits = (k + 1 + rows * kSplitU - 1) / (rows * kSplitU);
+  (void)units;
+  const int lanes = D * elem_bytes / 16;
+  DecodePlan plan{256, 0};
+  if (k + 1 <= (256 / lanes) * kBatch) return plan;
+  if (k + 1 <= (1024 / lanes) * kBatch) { plan.threads = 1024; return plan; }
+  const int chunk = (kPartThreads / lanes) * kBatch;
+  plan.splits = (k + 1 + chunk - 1) / chunk;
   return plan;
 }
 
-size_t decode_scratch_bytes(int elem_bytes, int D, int k, int units, size_t* counter_bytes) {
+size_t decode_scratch_bytes(int elem_bytes, int D, int k, int units) {
   const DecodePlan plan = plan_decode(elem_bytes, D, k, units);
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-  *counter_bytes = plan.splits ? up((size_t)units * 4) : 0;
   if (!plan.splits) return 0;
   return up((size_t)units * plan.splits * 2 * 4) + up((size_t)units * plan.splits * D * 4) +
          up((size_t)units * (k + 1) * 4);
 }
 
-SplitScratch carve_decode_scratch(int elem_bytes, int D, int k, int units, void* counters,
-                                  void* scratch) {
+SplitScratch carve_decode_scratch(int elem_bytes, int D, int k, int units, void* scratch) {
   const DecodePlan plan = plan_decode(elem_bytes, D, k, units);
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   char* b = static_cast<char*>(scratch);
   SplitScratch w{};
   w.splits = plan.splits;
-  w.counters = static_cast<int*>(counters);
   w.part_ml = reinterpret_cast<float*>(b);
   b += up((size_t)units * plan.splits * 2 * 4);
   w.part_o = reinterpret_cast<float*>(b);

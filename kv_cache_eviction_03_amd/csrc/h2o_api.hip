@@ -67,17 +67,16 @@ h2o_status check_desc(const h2o_cache_desc* c) {
 int units_of(const h2o_cache_desc* c) { return c->batch * c->heads; }
 int slots_of(const h2o_cache_desc* c) { return c->k_heavy + c->k_local; }
 
-// Workspace layout: [decode arrival counters | scratch]. The counters are used only by
-// the split decode, must be zero before its first use and are left zero by every call;
-// the scratch is shared by prefill (log-sum-exp + column sums) and decode (partials).
+// Workspace: scratch shared by prefill (log-sum-exp + column sums) and the split decode
+// (per-split partials and logits); its contents on entry never matter.
 size_t prefill_scratch(const h2o_cache_desc* c, int64_t T) {
   const size_t rows = (size_t)units_of(c) * (size_t)T;
   return 2 * round_up(rows * sizeof(float), kWsAlign);
 }
 
-size_t decode_scratch(const h2o_cache_desc* c, size_t* counter_bytes) {
+size_t decode_scratch(const h2o_cache_desc* c) {
   return h2o::decode_scratch_bytes((int)elem_bytes(c->dtype), c->head_dim, slots_of(c),
-                                   units_of(c), counter_bytes);
+                                   units_of(c));
 }
 
 h2o::DType dtype_of(const h2o_cache_desc* c) { return static_cast<h2o::DType>(c->dtype); }
@@ -103,9 +102,8 @@ const char* h2o_last_error(void) { return g_err; }
 
 size_t h2o_workspace_bytes(const h2o_cache_desc* c, int32_t max_prompt) {
   if (check_desc(c) != H2O_OK || max_prompt < 0) return 0;
-  size_t counters = 0;
-  const size_t a = prefill_scratch(c, max_prompt), b = decode_scratch(c, &counters);
-  return counters + (a > b ? a : b);
+  const size_t a = prefill_scratch(c, max_prompt), b = decode_scratch(c);
+  return a > b ? a : b;
 }
 
 h2o_status h2o_reset(const h2o_cache_desc* c, void* stream) {
@@ -132,9 +130,7 @@ h2o_status h2o_prefill(const h2o_cache_desc* c, const void* q, const void* k, co
   const int64_t units = (int64_t)c->batch * c->heads;
   if (units * (((int64_t)T + 15) / 16) > 0x7fffffffLL)
     return fail(H2O_ERR_UNSUPPORTED, "batch * heads * ceil(T / 16) exceeds the grid limit");
-  size_t counters = 0;
-  decode_scratch(c, &counters);
-  const size_t need = counters + prefill_scratch(c, T);
+  const size_t need = prefill_scratch(c, T);
   if (T > 0 && (!workspace || workspace_bytes < need))
     return fail(H2O_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
                 workspace ? workspace_bytes : (size_t)0, need);
@@ -143,7 +139,7 @@ h2o_status h2o_prefill(const h2o_cache_desc* c, const void* q, const void* k, co
   if (T == 0) return H2O_OK;
 
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace) + counters;
+  char* ws = static_cast<char*>(workspace);
   const size_t rows_bytes = round_up((size_t)units * T * sizeof(float), kWsAlign);
   float* lse2 = reinterpret_cast<float*>(ws);
   float* colsum = colsum_out ? colsum_out : reinterpret_cast<float*>(ws + rows_bytes);
@@ -183,20 +179,23 @@ h2o_status h2o_decode_step(const h2o_cache_desc* c, int64_t t, const void* q, co
               (aux->evicted_acc && !aligned(aux->evicted_acc, 4))))
     return fail(H2O_ERR_INVALID, "aux arrays must be 4-byte aligned");
 
-  size_t counters = 0;
-  const size_t scratch = decode_scratch(c, &counters);
-  if (counters + scratch > 0 && (!workspace || workspace_bytes < counters + scratch))
+  const h2o::DecodePlan plan =
+      h2o::plan_decode((int)elem_bytes(c->dtype), c->head_dim, slots_of(c), units_of(c));
+  if ((int64_t)units_of(c) * (plan.splits ? plan.splits : 1) > 0x7fffffffLL)
+    return fail(H2O_ERR_UNSUPPORTED, "batch * heads * %d decode workgroups exceed the grid limit",
+                plan.splits);
+  const size_t scratch = decode_scratch(c);
+  if (scratch > 0 && (!workspace || workspace_bytes < scratch))
     return fail(H2O_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
-                workspace ? workspace_bytes : (size_t)0, counters + scratch);
+                workspace ? workspace_bytes : (size_t)0, scratch);
   if (workspace && !aligned(workspace, kWsAlign))
     return fail(H2O_ERR_INVALID, "workspace must be %zu-byte aligned", kWsAlign);
 
   const int D = c->head_dim;
   const int32_t kk = c->k_heavy + c->k_local;
   const h2o::SplitScratch w =
-      counters ? h2o::carve_decode_scratch((int)elem_bytes(c->dtype), D, kk, units_of(c),
-                                           workspace, static_cast<char*>(workspace) + counters)
-               : h2o::SplitScratch{};
+      scratch ? h2o::carve_decode_scratch((int)elem_bytes(c->dtype), D, kk, units_of(c), workspace)
+              : h2o::SplitScratch{};
   h2o::DecodeParams p{q, k_new, v_new, c->k_slots, c->v_slots, c->slot_pos, c->acc_score, out,
                       aux ? aux->victim_slot : nullptr, aux ? aux->evicted_pos : nullptr,
                       aux ? aux->evicted_acc : nullptr, (int32_t)(c->batch * c->heads), kk,

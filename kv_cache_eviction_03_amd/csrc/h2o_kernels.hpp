@@ -61,28 +61,25 @@ struct ResetParams {
   int64_t n;            // units * k
 };
 
-// Decode launch plan: splits == 0 -> one resident workgroup per unit holding u slot
-// batches; splits > 0 -> `splits` workgroups per unit of kSplitU batches each.
-constexpr int kSplitU = 8;
+// Decode launch plan: splits == 0 -> one resident workgroup of `threads` threads per
+// unit; splits > 0 -> a partial kernel with `splits` workgroups per unit, then a
+// combine kernel with one workgroup per unit.
 struct DecodePlan {
-  int u;
+  int threads;
   int splits;
 };
 DecodePlan plan_decode(int elem_bytes, int D, int k, int units);
+constexpr int kMaxSplits = 160;   // enough for k <= 8192 at 64 slots per split
 
-// Workspace of the split decode: per-unit arrival counters (zero between calls) and
-// per-split partials plus the step's logits.
+// Workspace of the split decode: per-split partials plus the step's logits.
 struct SplitScratch {
-  int* counters;        // [units]
   float* part_ml;       // [units][splits][2]  (max, sum) in the log2 domain
   float* part_o;        // [units][splits][D]  unnormalised output
   float* logits;        // [units][k + 1]
   int splits;
 };
-// Bytes of the scratch part; *counter_bytes receives the size of the counter part.
-size_t decode_scratch_bytes(int elem_bytes, int D, int k, int units, size_t* counter_bytes);
-SplitScratch carve_decode_scratch(int elem_bytes, int D, int k, int units, void* counters,
-                                  void* scratch);
+size_t decode_scratch_bytes(int elem_bytes, int D, int k, int units);
+SplitScratch carve_decode_scratch(int elem_bytes, int D, int k, int units, void* scratch);
 
 hipError_t launch_reset(const ResetParams& p, hipStream_t s);
 hipError_t launch_decode(DType dt, int D, const DecodeParams& p, const SplitScratch& w,

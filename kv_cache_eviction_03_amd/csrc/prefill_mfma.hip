@@ -40,9 +40,21 @@ template <typename T> __device__ __forceinline__ typename Vec8<T>::type ld8(cons
   return *reinterpret_cast<const typename Vec8<T>::type*>(p);
 }
 
+// LDS row strides. K/Q tiles are read 16 bytes per lane, one row per lane: a stride of
+// D + 8 elements (4 dwords past a multiple of 32 banks) spreads consecutive rows over
+// distinct banks. The V tile is read with the transposing 8-byte read, four 32-byte row
+// segments per 16-lane group: a stride of D + 16 (8 dwords past a multiple of 32) puts
+// those four segments in disjoint banks.
+#ifndef H2O_KPAD
+#define H2O_KPAD 8
+#endif
+#ifndef H2O_VPAD
+#define H2O_VPAD 16
+#endif
 template <int D> struct Tile {
   static constexpr int CPR = D / 8;                  // 16-byte chunks per row
-  static constexpr int KS = D + 8;                   // row-major tile stride (elements)
+  static constexpr int KS = D + H2O_KPAD;            // K / Q tile stride (elements)
+  static constexpr int VS = D + H2O_VPAD;            // V tile stride (elements)
   static constexpr int KCH = BN * CPR / kThreads;    // row chunks per thread
 };
 
@@ -69,11 +81,12 @@ struct RowTile {
       c[i] = v;
     }
   }
+  template <int STRIDE>
   __device__ __forceinline__ void store(T* tile, int tid) const {
 #pragma unroll
     for (int i = 0; i < Tile<D>::KCH; ++i) {
       const int ch = tid + i * kThreads, row = ch / Tile<D>::CPR, cc = ch % Tile<D>::CPR;
-      st16(tile + row * Tile<D>::KS + cc * 8, c[i]);
+      st16(tile + row * STRIDE + cc * 8, c[i]);
     }
   }
 };
@@ -107,9 +120,9 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p)
   using V4 = typename Vec8<T>::half;
   constexpr bool kSplit = !__is_same(T, _Float16);
   constexpr int BM = kWaves * 16 * RB;
-  constexpr int KS = Tile<D>::KS;
+  constexpr int KS = Tile<D>::KS, VS = Tile<D>::VS;
   __shared__ __attribute__((aligned(16))) T k_tile[BN * KS];
-  __shared__ __attribute__((aligned(16))) T v_tile[BN * KS];
+  __shared__ __attribute__((aligned(16))) T v_tile[BN * VS];
 
   const int T_ = p.T;
   const int nqb = (T_ + BM - 1) / BM;
@@ -157,8 +170,8 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p)
   for (int kt = 0; kt < nkt; ++kt) {
     const int key0 = kt * BN;
     if constexpr (PREFETCH) {
-      kreg.store(k_tile, tid);
-      vreg.store(v_tile, tid);
+      kreg.template store<KS>(k_tile, tid);
+      vreg.template store<VS>(v_tile, tid);
       __syncthreads();
       if (kt + 1 < nkt) {
         kreg.load(K, key0 + BN, T_, tid);
@@ -168,8 +181,8 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p)
     } else {
       kreg.load(K, key0, T_, tid);
       vreg.load(V, key0, T_, tid);
-      kreg.store(k_tile, tid);
-      vreg.store(v_tile, tid);
+      kreg.template store<KS>(k_tile, tid);
+      vreg.template store<VS>(v_tile, tid);
       __syncthreads();
     }
     // Only tiles that reach past the wave's first row need the causal mask.
@@ -257,9 +270,9 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p)
       for (int db = 0; db < D / 16; ++db) {
         // keys ks*32 + 4g + r (then + 16) of dim db*16 + l16: lane 4r + q of each
         // 16-lane group points at V[key][db*16 + 4q]
-        const T* vr = v_tile + (ks * 32 + 4 * g + (l16 >> 2)) * KS + db * 16 + 4 * (l16 & 3);
+        const T* vr = v_tile + (ks * 32 + 4 * g + (l16 >> 2)) * VS + db * 16 + 4 * (l16 & 3);
         const V4 lo = TrRead<T>::read(vr);
-        const V4 hi = TrRead<T>::read(vr + 16 * KS);
+        const V4 hi = TrRead<T>::read(vr + 16 * VS);
         const V8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
@@ -336,7 +349,7 @@ __global__ __launch_bounds__(kThreads) void prefill_colsum_kernel(PrefillParams 
   for (int qt = qt0; qt < nq; ++qt) {
     const int q0 = qt * BN;
     if constexpr (PREFETCH) {
-      qreg.store(q_tile, tid);
+      qreg.template store<KS>(q_tile, tid);
       if (tid < BN) lse_tile[tid] = lreg;
       __syncthreads();
       if (qt + 1 < nq) {
@@ -347,7 +360,7 @@ __global__ __launch_bounds__(kThreads) void prefill_colsum_kernel(PrefillParams 
     } else {
       qreg.load(Q, q0, T_, tid);
       if (tid < BN) lreg = q0 + tid < T_ ? lse[q0 + tid] : 0.f;
-      qreg.store(q_tile, tid);
+      qreg.template store<KS>(q_tile, tid);
       if (tid < BN) lse_tile[tid] = lreg;
       __syncthreads();
     }

@@ -64,6 +64,10 @@ SMALL = [
     Workload(96, "t1-f32-d64", 1, 1, 1, 64, "f32", 1, 6, 1, 1),
     # prompt of exactly two tiles, bf16 d=128, several heavy hitters
     Workload(97, "tiles-bf16", 1, 1, 4, 128, "bf16", 128, 16, 20, 12, heavy_frac=0.05, sinks=4),
+    # fp32 d=128 with k = 300: the split decode (five 64-slot chunks, then the combine)
+    Workload(88, "split-f32-d128", 1, 1, 2, 128, "f32", 280, 40, 150, 150),
+    # bf16 d=64 with k = 1500: six 256-slot chunks; 1024-thread combine loops over slots
+    Workload(89, "split-bf16-d64", 1, 1, 2, 64, "bf16", 1400, 150, 750, 750, heavy_frac=0.05),
 ]
 
 
