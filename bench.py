@@ -20,7 +20,9 @@ Timing:
   * graph replays are checked bit for bit against an eager run;
   * cpu_baseline: the CPU oracle on the same inputs (all 256 units of one step);
   * prefill_mfma_opt30b: the prefill of the OPT-30B-shaped layer (T = 2048), where
-    prefill is MFMA-bound, against the 2.5 PFLOP/s dense fp16 peak.
+    prefill is MFMA-bound, against the 2.5 PFLOP/s dense fp16 peak;
+  * decode_by_workload: the decode kernel at each workload's layer shape (the
+    LLaMA-7B layer, the OPT-30B layer, the 4096-slot stream), graph-replayed.
 """
 from __future__ import annotations
 
@@ -43,8 +45,8 @@ METRIC = "H2O decode tokens/s at 20% KV budget + % of HBM roofline (prefill % MF
 # is recorded with them, and the figure is reported only while the sources still match.
 DECODE_SOURCES = ("kv_cache_eviction_03_amd/csrc/decode.hip",
                   "kv_cache_eviction_03_amd/csrc/h2o_device.hpp")
-DECODE_TRAFFIC = {"sha256": "28b2e6bf6590326ae489984d2a3bffd860cc43eec95abed3b79eef588e82edcf",
-                  "read_bytes": 14180754, "write_bytes": 376832}
+DECODE_TRAFFIC = {"sha256": "aaa7f8d9b338cb16a8eca4f1e654e2f4d95889659a8b5259f850a425e98e0a6c",
+                  "read_bytes": 14165395, "write_bytes": 376832}
 
 
 def decode_sources_hash() -> str:
@@ -117,6 +119,57 @@ def prefill_mfma_probe(reps=3):
     return res
 
 
+def decode_by_workload(ids=(2, 3, 4, 5), n=32, reps=5):
+    """Decode launches of each workload's layer shape, graph-replayed, timed with HIP events.
+
+    The cache is filled by a prefill of k + 64 tokens (so every step evicts), then n
+    decode steps are captured once and replayed; the best replay's mean per launch is
+    reported with the algorithmic bytes of one launch.
+    """
+    import torch
+
+    from kv_cache_eviction_03_amd import H2OCache
+    from workloads import WORKLOADS, generate
+    dev = "cuda:0"
+    res = []
+    for wid in ids:
+        w = WORKLOADS[wid].scaled(prompt=WORKLOADS[wid].k + 64, steps=n, layers=1)
+        x = generate(w, seed=0, device=dev)
+        c = H2OCache(w.batch, w.heads, w.head_dim, w.k_heavy, w.k_local, w.torch_dtype, dev,
+                     max_prompt=w.prompt)
+        out = torch.empty((n, w.batch, w.heads, w.head_dim), dtype=torch.float32, device=dev)
+        c.reset()
+        c.prefill(x["q_prompt"], x["k_prompt"], x["v_prompt"])
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream(dev)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for i in range(n):
+                    c.decode(x["q_dec"][i], x["k_dec"][i], x["v_dec"][i], out=out[i])
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(reps):
+            c.reset()
+            c.prefill(x["q_prompt"], x["k_prompt"], x["v_prompt"])
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            us = 1e3 * a.elapsed_time(b) / n
+            best = us if best is None else min(best, us)
+        byt = decode_bytes_per_unit(w) * w.units_per_layer
+        res.append({"workload": f"{w.name} layer: B {w.batch}, H {w.heads}, d {w.head_dim}, "
+                                f"{w.dtype}, k = {w.k_heavy}+{w.k_local}",
+                    "us_per_launch": best, "algorithmic_MB": byt / 1e6,
+                    "GBps": byt / (best * 1e-6) / 1e9, "hbm_frac": byt / (best * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                    "decode_tokens_per_s": w.batch / (best * 1e-6)})
+        del x, c, out, g
+        torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(w, x, units):
     import numpy as np
     from threadpoolctl import threadpool_info
@@ -147,6 +200,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mfma-probe", action="store_true")
+    ap.add_argument("--decode-shapes", action="store_true",
+                    help="only time the decode kernel at each workload's layer shape")
+    ap.add_argument("--no-decode-shapes", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 512 MiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -165,6 +221,11 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 3}))
+        return
+
+    if args.decode_shapes:
+        for r in decode_by_workload():
+            print(json.dumps(r), flush=True)
         return
 
     from kv_cache_eviction_03_amd import H2OCache
@@ -299,6 +360,8 @@ def main():
     }
     if not args.no_mfma_probe:
         result["prefill_mfma_opt30b"] = prefill_mfma_probe()
+    if not args.no_decode_shapes:
+        result["decode_by_workload"] = decode_by_workload()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, x, list(range(units)))
     print(json.dumps(result), flush=True)

@@ -25,9 +25,10 @@
 // Kernels:
 //   * resident: one workgroup per unit (256 or 1024 threads) when the unit fits
 //     one load batch (k + 1 <= ROWS * 8). Row groups publish (max, sum,
-//     unnormalised out) in LDS; wave 0 turns them into scale factors; owners
-//     update their scores and the (acc, pos) minimum is a wave minimum plus an
-//     LDS stage. Three barriers, no global scratch.
+//     unnormalised out) in LDS; every wave folds them into scale factors with
+//     wave-uniform DPP reductions (the factors reach the output loop as scalars);
+//     owners update their scores and the (acc, pos) minimum is a wave fold plus
+//     an LDS stage. Two barriers, no global scratch.
 //   * split: for larger k, two launches. split_partial gives S workgroups per
 //     unit one slot chunk each and writes (max, sum, unnormalised out) plus the
 //     chunk's logits to the workspace; split_combine (one 1024-thread workgroup
@@ -131,29 +132,6 @@ __device__ __forceinline__ uint64_t score_key(float a, int pos) {
 }
 
 
-// Row-group partials in LDS -> per-group scale factors 2^(m_g - M), the global max M
-// and 1 / sum, computed once by wave 0 (fixed order) and published in LDS.
-template <int ROWS>
-__device__ __forceinline__ void combine_groups(const float* s_m, const float* s_l, float* s_sc,
-                                               float* s_stat, int tid) {
-  static_assert(ROWS <= 2 * kWave, "at most two row groups per lane of wave 0");
-  if (tid < kWave) {
-    float m = -INFINITY;
-#pragma unroll
-    for (int r = tid; r < ROWS; r += kWave) m = fmaxf(m, s_m[r]);
-    m = group_max<kWave>(m);
-    float l = 0.f;
-#pragma unroll
-    for (int r = tid; r < ROWS; r += kWave) {
-      const float sc = s_m[r] == -INFINITY ? 0.f : fast_exp2(s_m[r] - m);
-      s_sc[r] = sc;
-      l = fmaf(s_l[r], sc, l);
-    }
-    l = group_sum<kWave>(l);
-    if (tid == 0) { s_stat[0] = m; s_stat[1] = 1.0f / l; }
-  }
-}
-
 // ------------------------------------------------------------------ resident --
 
 template <typename T, int D, int THREADS>
@@ -162,7 +140,7 @@ __global__ __launch_bounds__(THREADS) void decode_resident_kernel(DecodeParams p
   constexpr int VEC = S::VEC, LANES = S::LANES, ROWS = S::ROWS, U = kBatch;
   static_assert(U <= LANES, "a lane owns one slot score");
   __shared__ __attribute__((aligned(16))) float s_red[ROWS * D];
-  __shared__ float s_m[ROWS], s_l[ROWS], s_sc[ROWS], s_stat[2];
+  __shared__ float s_m[ROWS], s_l[ROWS];
   __shared__ float s_logit[ROWS * U];
   __shared__ uint64_t s_key[S::WAVES];
 
@@ -205,37 +183,27 @@ __global__ __launch_bounds__(THREADS) void decode_resident_kernel(DecodeParams p
     for (int u = 0; u < U; ++u) s_logit[u * ROWS + g] = s[u];
   }
   __syncthreads();                              // (1) every K/V read is consumed
-  // Scale factors 2^(m_g - M) of the row groups. With few groups every thread forms
-  // them itself in registers (no extra barrier); with many, wave 0 forms them once.
-  float M, inv;
-  float sc[ROWS <= 16 ? ROWS : 1];
-  if constexpr (ROWS <= 16) {
-    M = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < ROWS; ++r) M = fmaxf(M, s_m[r]);
-    float L = 0.f;
-#pragma unroll
-    for (int r = 0; r < ROWS; ++r) {
-      sc[r] = s_m[r] == -INFINITY ? 0.f : fast_exp2(s_m[r] - M);
-      L = fmaf(s_l[r], sc[r], L);
-    }
-    inv = 1.0f / L;
-  } else {
-    combine_groups<ROWS>(s_m, s_l, s_sc, s_stat, tid);
-    __syncthreads();                            // (2)
-    M = s_stat[0];
-    inv = s_stat[1];
-  }
+  // Scale factors 2^(m_g - M) of the row groups, formed by every wave for itself with
+  // wave-uniform folds: lane r holds group r (and r + 64), one exp2 per lane, and the
+  // factors reach the output loop as scalars through readlane.
+  static_assert(ROWS <= 2 * kWave, "at most two row groups per lane");
+  const float m_a = lane < ROWS ? s_m[lane] : -INFINITY;
+  const float m_b = lane + kWave < ROWS ? s_m[lane + kWave] : -INFINITY;
+  const float M = wave_max_uniform(fmaxf(m_a, m_b));
+  const float sc_a = m_a == -INFINITY ? 0.f : fast_exp2(m_a - M);
+  const float sc_b = m_b == -INFINITY ? 0.f : fast_exp2(m_b - M);
+  const float l_ab = (lane < ROWS ? s_l[lane] * sc_a : 0.f) +
+                     (lane + kWave < ROWS ? s_l[lane + kWave] * sc_b : 0.f);
+  const float inv = __builtin_amdgcn_rcpf(wave_sum_uniform(l_ab));
   const float p_new = fast_exp2(s_logit[n] - M) * inv;
 
   for (int c = tid; c < D; c += THREADS) {
     float v = 0.f;
-    if constexpr (ROWS <= 16) {
 #pragma unroll
-      for (int r = 0; r < ROWS; ++r) v = fmaf(s_red[r * D + c], sc[r], v);
-    } else {
-#pragma unroll 8
-      for (int r = 0; r < ROWS; ++r) v = fmaf(s_red[r * D + c], s_sc[r], v);
+    for (int r = 0; r < ROWS; ++r) {
+      const float scr = __uint_as_float(__builtin_amdgcn_readlane(
+          (int)__float_as_uint(r < kWave ? sc_a : sc_b), r % kWave));
+      v = fmaf(s_red[r * D + c], scr, v);
     }
     p.out[(size_t)unit * D + c] = v * inv;
   }
@@ -247,9 +215,9 @@ __global__ __launch_bounds__(THREADS) void decode_resident_kernel(DecodeParams p
     acc[jo] = a;
     if (full && pos_old <= limit) key = score_key(a, pos_old);
   }
-  const uint64_t wmin = wave_min_u64(key);
+  const uint64_t wmin = wave_min_u64_uniform(key);
   if (lane == 0) s_key[wave] = wmin;
-  __syncthreads();                              // (3)
+  __syncthreads();                              // (2)
   uint64_t best = s_key[0];
 #pragma unroll
   for (int w = 1; w < S::WAVES; ++w) best = s_key[w] < best ? s_key[w] : best;

@@ -94,6 +94,42 @@ __device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
   return v;
 }
 
+// Wave-wide reductions whose result every lane receives as a uniform value: DPP steps
+// inside each 16-lane row, then row_bcast15 / row_bcast31 fold the rows into lane 63,
+// then readlane. The combination order is fixed, so the result is reproducible.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_or(uint32_t old, uint32_t v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xf, false);
+}
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_fold_u32(uint32_t v, uint32_t identity, Op op) {
+  v = op(v, dpp_or<0xb1, 0xf>(identity, v));     // quad_perm [1,0,3,2]
+  v = op(v, dpp_or<0x4e, 0xf>(identity, v));     // quad_perm [2,3,0,1]
+  v = op(v, dpp_or<0x141, 0xf>(identity, v));    // row_half_mirror
+  v = op(v, dpp_or<0x140, 0xf>(identity, v));    // row_mirror: every lane has its row's value
+  v = op(v, dpp_or<0x142, 0xa>(identity, v));    // row_bcast15 into rows 1 and 3
+  v = op(v, dpp_or<0x143, 0xc>(identity, v));    // row_bcast31 into rows 2 and 3
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ __forceinline__ float wave_max_uniform(float v) {
+  return __uint_as_float(wave_fold_u32(__float_as_uint(v), __float_as_uint(-INFINITY),
+      [](uint32_t a, uint32_t b) { return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b))); }));
+}
+__device__ __forceinline__ float wave_sum_uniform(float v) {
+  return __uint_as_float(wave_fold_u32(__float_as_uint(v), 0u,
+      [](uint32_t a, uint32_t b) { return __float_as_uint(__uint_as_float(a) + __uint_as_float(b)); }));
+}
+__device__ __forceinline__ uint32_t wave_min_u32_uniform(uint32_t v) {
+  return wave_fold_u32(v, ~0u, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+}
+// Minimum of 64-bit keys over the wave as two 32-bit folds (high word, then the low word
+// among lanes holding that high word).
+__device__ __forceinline__ uint64_t wave_min_u64_uniform(uint64_t v) {
+  const uint32_t hi = wave_min_u32_uniform((uint32_t)(v >> 32));
+  const uint32_t lo = wave_min_u32_uniform((uint32_t)(v >> 32) == hi ? (uint32_t)v : ~0u);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 // 16x16x32 MFMA, fp32 accumulate (gfx950). Lane l supplies A[l%16][k-group l/16]
 // and B[k-group l/16][l%16]; D[4*(l/16)+i][l%16] comes back in element i.
 __device__ __forceinline__ f32x4 mfma16x16x32(const f16x8& a, const f16x8& b, const f32x4& c) {
