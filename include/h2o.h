@@ -144,6 +144,9 @@ size_t h2o_workspace_bytes(const h2o_cache_desc* cache, int32_t max_prompt);
  * higher) are kept. Kept positions fill slots 0.. in ascending position order
  * (K/V rows copied from k and v, slot_pos = position, acc_score = fp32 c_j);
  * every other slot is marked free. All previous slot contents are replaced.
+ * Returns H2O_ERR_UNSUPPORTED when one unit's prompt rows exceed 2^31 - 1 bytes
+ * (T * head_dim * element size) or the launch grid would exceed 2^31 - 1
+ * workgroups; nothing is enqueued then.
  */
 h2o_status h2o_prefill(const h2o_cache_desc* cache, const void* q, const void* k,
                        const void* v, int32_t T, float* out, float* colsum_out,

@@ -128,8 +128,12 @@ h2o_status h2o_prefill(const h2o_cache_desc* c, const void* q, const void* k, co
   if (colsum_out && !aligned(colsum_out, 4))
     return fail(H2O_ERR_INVALID, "colsum_out must be 4-byte aligned");
   const int64_t units = (int64_t)c->batch * c->heads;
-  if (units * (((int64_t)T + 15) / 16) > 0x7fffffffLL)
+  if (h2o::xcd_grid_blocks(units, ((int64_t)T + 15) / 16) > 0x7fffffffLL)
     return fail(H2O_ERR_UNSUPPORTED, "batch * heads * ceil(T / 16) exceeds the grid limit");
+  // The attention kernels address one unit's K/V rows through a buffer descriptor whose
+  // byte range is a signed 32-bit count.
+  if ((int64_t)T * c->head_dim * (int64_t)elem_bytes(c->dtype) > 0x7fffffffLL)
+    return fail(H2O_ERR_UNSUPPORTED, "T * head_dim * element size exceeds 2^31 - 1 bytes");
   const size_t need = prefill_scratch(c, T);
   if (T > 0 && (!workspace || workspace_bytes < need))
     return fail(H2O_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",

@@ -10,6 +10,36 @@ namespace h2o {
 
 enum class DType : int { F32 = 0, F16 = 1, BF16 = 2 };
 
+// Prefill block numbering. MI355X hands workgroups to its 8 XCDs round-robin by block
+// index, and each XCD has its own L2. A unit (sequence, head) has `per_unit` blocks that
+// read the same K/V (or Q) rows, so a unit's blocks all go to XCD unit % 8. Each XCD takes
+// its units in groups of about one resident round (~64 workgroups: 32 CUs x 2) and issues
+// a group's blocks block-index-major, so the longest blocks of the group start first (r = 0
+// is the longest) while the group's blocks share L2. Units are padded to whole groups;
+// blocks of padding units exit at once.
+constexpr int kXcds = 8;
+__host__ __device__ inline int xcd_group_units(int64_t units, int per_unit) {
+  const int64_t per_xcd = (units + kXcds - 1) / kXcds;
+  int64_t g = (64 + per_unit - 1) / per_unit;
+  if (g > per_xcd) g = per_xcd;
+  return g < 1 ? 1 : (int)g;
+}
+inline int64_t xcd_grid_blocks(int64_t units, int per_unit) {
+  const int64_t g = xcd_group_units(units, per_unit);
+  const int64_t groups = (units + kXcds * g - 1) / (kXcds * g);
+  return groups * kXcds * g * per_unit;
+}
+// Inverse of that numbering: block `bid` works on block `r` of unit `unit`; unit >= units
+// marks a padding block.
+struct UnitBlock { int unit, r; };
+__device__ __forceinline__ UnitBlock xcd_unit_block(int bid, int units, int per_unit) {
+  const int g = xcd_group_units(units, per_unit);
+  const int x = bid & 7, j = bid >> 3;
+  const int grp = j / (g * per_unit), w = j - grp * (g * per_unit);
+  const int r = w / g;
+  return {(grp * g + (w - r * g)) * 8 + x, r};
+}
+
 struct DecodeParams {
   const void* q;        // [units][D]
   const void* k_new;    // [units][D]

@@ -18,20 +18,24 @@
 // again belong to query l%16, so the online rescale is lane-local.
 //
 // Tiling: each wave holds RB blocks of 16 rows, so every operand read from LDS
-// feeds RB MFMAs; the next key (or query) tile is loaded into registers while
-// the current one is consumed from LDS. K and V tiles sit row-major in LDS
-// (rows padded by 16 bytes); the V operand of the PV product is fetched with
-// gfx950's transposing LDS read, so V needs no register transpose.
+// feeds RB MFMAs. Tiles are copied straight from global memory into
+// double-buffered LDS (buffer_load ... lds), so the next tile's loads are in
+// flight while the current one is consumed and one barrier per tile suffices.
+// Tile rows are unpadded with XOR-swizzled 16-byte chunks; the V operand of the
+// PV product is fetched with gfx950's transposing LDS read, so V needs no
+// register transpose.
 //
 // bf16: P rounded to bf16 alone gives up to ~3e-3 abs error on O for N(0,1)
 // data, so P is split into a bf16 high part and a bf16 residual, two MFMAs.
 #include "h2o_device.hpp"
 #include "h2o_kernels.hpp"
 
+#include <type_traits>
+
 namespace h2o {
 namespace {
 
-constexpr int BN = 64;    // keys per tile (attention) / queries per tile (column sums)
+constexpr int BN = 64;    // queries per column-sum tile
 constexpr float kLazy = 8.f;  // log2-domain slack before the running max is moved
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
@@ -39,57 +43,6 @@ constexpr int kWaves = kThreads / kWave;
 template <typename T> __device__ __forceinline__ typename Vec8<T>::type ld8(const T* p) {
   return *reinterpret_cast<const typename Vec8<T>::type*>(p);
 }
-
-// LDS row strides. K/Q tiles are read 16 bytes per lane, one row per lane: a stride of
-// D + 8 elements (4 dwords past a multiple of 32 banks) spreads consecutive rows over
-// distinct banks. The V tile is read with the transposing 8-byte read, four 32-byte row
-// segments per 16-lane group: a stride of D + 16 (8 dwords past a multiple of 32) puts
-// those four segments in disjoint banks.
-#ifndef H2O_KPAD
-#define H2O_KPAD 8
-#endif
-#ifndef H2O_VPAD
-#define H2O_VPAD 16
-#endif
-template <int D> struct Tile {
-  static constexpr int CPR = D / 8;                  // 16-byte chunks per row
-  static constexpr int KS = D + H2O_KPAD;            // K / Q tile stride (elements)
-  static constexpr int VS = D + H2O_VPAD;            // V tile stride (elements)
-  static constexpr int KCH = BN * CPR / kThreads;    // row chunks per thread
-};
-
-// One BN-row tile of a [T][D] matrix, held in registers between the global load
-// and the LDS store. Rows past T are loaded from row T-1 and zeroed.
-template <typename T, int D>
-struct RowTile {
-  uint4 c[Tile<D>::KCH];
-  __device__ __forceinline__ void load(const T* src, int row0, int T_, int tid) {
-    if (row0 + BN <= T_) {                       // whole tile in range
-#pragma unroll
-      for (int i = 0; i < Tile<D>::KCH; ++i) {
-        const int ch = tid + i * kThreads, row = ch / Tile<D>::CPR, cc = ch % Tile<D>::CPR;
-        c[i] = ld16(src + (size_t)(row0 + row) * D + cc * 8);
-      }
-      return;
-    }
-#pragma unroll
-    for (int i = 0; i < Tile<D>::KCH; ++i) {
-      const int ch = tid + i * kThreads, row = ch / Tile<D>::CPR, cc = ch % Tile<D>::CPR;
-      const int r = row0 + row;
-      uint4 v = ld16(src + (size_t)(r < T_ ? r : T_ - 1) * D + cc * 8);
-      if (r >= T_) v = make_uint4(0, 0, 0, 0);
-      c[i] = v;
-    }
-  }
-  template <int STRIDE>
-  __device__ __forceinline__ void store(T* tile, int tid) const {
-#pragma unroll
-    for (int i = 0; i < Tile<D>::KCH; ++i) {
-      const int ch = tid + i * kThreads, row = ch / Tile<D>::CPR, cc = ch % Tile<D>::CPR;
-      st16(tile + row * STRIDE + cc * 8, c[i]);
-    }
-  }
-};
 
 // Transposed LDS read (gfx950 ds_read_b64_tr_b16). Within each 16-lane group the 16
 // lanes' 4-element reads form 4 rows of 16 elements (row r = lanes 4r..4r+3 in
@@ -114,28 +67,97 @@ template <> struct TrRead<__bf16> {
   }
 };
 
-template <typename T, int D, int RB, bool PREFETCH>
-__global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p) {
+// ---------------------------------------------------------------------------------
+// Direct-to-LDS tiles. buffer_load_dwordx4 ... lds (gfx950) writes each lane's 16 bytes
+// to LDS at M0 + 16 * lane, so one wave instruction fills 1 KB of LDS with no register
+// staging. Tile rows are unpadded; instead the 16-byte chunks of a row are XOR-swizzled
+// so that the MFMA operand reads stay conflict-free. Rows at or past T fall outside the
+// buffer descriptor's range and read as zero.
+constexpr int kRsrcWord3 = 0x00020000;   // gfx9 untyped buffer access (32-bit data format)
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+#ifndef H2O_ATTN_BN
+#define H2O_ATTN_BN 32
+#endif
+constexpr int BNA = H2O_ATTN_BN;   // keys per attention tile
+
+template <typename T, int D, int ROWS> struct DTile {
+  static constexpr int ROW = D * (int)sizeof(T);             // bytes per row
+  static constexpr int CPR = ROW / 16;                        // 16-byte chunks per row
+  static constexpr int BYTES = ROWS * ROW;                    // bytes per tile
+  static constexpr int NI = BYTES / (kThreads * 16);          // loads per thread per tile
+  static_assert(NI >= 1 && BYTES % (kThreads * 16) == 0, "tile must be whole 16-byte loads per thread");
+};
+// K tiles feed the A operand of S^T = K Q^T: 16 lanes read one chunk of 16 consecutive
+// rows, so chunk c of row r is stored at c ^ (r % CPR).
+template <int CPR> __device__ __forceinline__ int swz_k(int row, int c) { return c ^ (row & (CPR - 1)); }
+// V tiles feed the transposing 8-byte reads: 16 lanes read 32 bytes of 4 consecutive
+// rows, so chunk c of row r is stored at c ^ 2 * (r % (CPR / 2)).
+template <int CPR> __device__ __forceinline__ int swz_v(int row, int c) { return c ^ ((row & (CPR / 2 - 1)) << 1); }
+
+template <typename T, int D, int ROWS, bool V_LAYOUT>
+struct TileDma {
+  using G = DTile<T, D, ROWS>;
+  uint32_t voff[G::NI];   // byte offset in the source rows of each of this lane's loads
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < G::NI; ++i) {
+      const int L = (wave * G::NI + i) * kWave + lane;        // LDS chunk this lane fills
+      const int row = L / G::CPR, c = L % G::CPR;
+      const int src_c = V_LAYOUT ? swz_v<G::CPR>(row, c) : swz_k<G::CPR>(row, c);
+      voff[i] = (uint32_t)(row * G::ROW + src_c * 16);
+    }
+  }
+  // Rows [row0, row0 + ROWS) of a [T][D] matrix into `tile`.
+  __device__ __forceinline__ void issue(const T* src, int row0, int T_, char* tile, int wave) const {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T*>(src + (size_t)row0 * D), (short)0, (T_ - row0) * G::ROW, kRsrcWord3);
+#pragma unroll
+    for (int i = 0; i < G::NI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (lds_ptr)(tile + (wave * G::NI + i) * (kWave * 16)), 16, voff[i], 0, 0, 0);
+  }
+};
+
+// Max of a value over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four lanes that hold one query
+// row of an S^T accumulator), with the gfx950 lane-swap instructions.
+__device__ __forceinline__ float quad_row_max(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Causal attention of query block qb (BM rows) of one unit over all keys up to the block's
+// last row. K and V tiles are double-buffered in LDS (kbuf / vbuf hold two tiles each):
+// the loads of tile kt + 1 are in flight while tile kt is consumed, and one barrier per
+// tile separates the buffer generations.
+template <typename T, int D, int RB>
+__device__ __forceinline__ void attn_block(const PrefillParams& p, int unit, int qb,
+                                           char* kbuf, char* vbuf) {
   using V8 = typename Vec8<T>::type;
   using V4 = typename Vec8<T>::half;
+  using G = DTile<T, D, BNA>;
   constexpr bool kSplit = !__is_same(T, _Float16);
   constexpr int BM = kWaves * 16 * RB;
-  constexpr int KS = Tile<D>::KS, VS = Tile<D>::VS;
-  __shared__ __attribute__((aligned(16))) T k_tile[BN * KS];
-  __shared__ __attribute__((aligned(16))) T v_tile[BN * VS];
-
   const int T_ = p.T;
-  const int nqb = (T_ + BM - 1) / BM;
-  const int r = blockIdx.x / p.units;          // longest rows first
-  const int unit = blockIdx.x - r * p.units;
-  const int qb = nqb - 1 - r;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
   const size_t base = (size_t)unit * T_ * D;
   const T* Q = static_cast<const T*>(p.q) + base;
   const T* K = static_cast<const T*>(p.k) + base;
   const T* V = static_cast<const T*>(p.v) + base;
   const int row0 = qb * BM + wave * 16 * RB;    // this wave's first row
+
+  TileDma<T, D, BNA, false> kdma;
+  TileDma<T, D, BNA, true> vdma;
+  kdma.init(wave, lane);
+  vdma.init(wave, lane);
+  const int kend = min(T_, (qb + 1) * BM);
+  const int nkt = (kend + BNA - 1) / BNA;
+  kdma.issue(K, 0, T_, kbuf, wave);
+  vdma.issue(V, 0, T_, vbuf, wave);
 
   V8 qa[RB][D / 32];
 #pragma unroll
@@ -148,7 +170,6 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p)
       qa[rb][kk] = v;
     }
   }
-
   f32x4 o[RB][D / 16];
   float m[RB], ls[RB];
 #pragma unroll
@@ -158,128 +179,154 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p)
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  // Tiles past this wave's last row are not computed (their loads are still issued).
+  const int wlast = (min(row0 + 16 * RB, kend) - 1) / BNA;
+  __syncthreads();                              // tile 0 landed
 
-  const int kend = min(T_, (qb + 1) * BM);
-  const int nkt = (kend + BN - 1) / BN;
-  RowTile<T, D> kreg, vreg;
-  if constexpr (PREFETCH) {
-    kreg.load(K, 0, T_, tid);
-    vreg.load(V, 0, T_, tid);
-  }
-
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int key0 = kt * BN;
-    if constexpr (PREFETCH) {
-      kreg.template store<KS>(k_tile, tid);
-      vreg.template store<VS>(v_tile, tid);
-      __syncthreads();
-      if (kt + 1 < nkt) {
-        kreg.load(K, key0 + BN, T_, tid);
-        vreg.load(V, key0 + BN, T_, tid);
-      }
-      __builtin_amdgcn_sched_barrier(0);        // next tile's loads go out first
-    } else {
-      kreg.load(K, key0, T_, tid);
-      vreg.load(V, key0, T_, tid);
-      kreg.template store<KS>(k_tile, tid);
-      vreg.template store<VS>(v_tile, tid);
-      __syncthreads();
+  // Next tile's loads go into the buffers freed by the last barrier.
+  auto prefetch = [&](int kt) {
+    if (kt + 1 < nkt) {
+      kdma.issue(K, (kt + 1) * BNA, T_, kbuf + ((kt + 1) & 1) * G::BYTES, wave);
+      vdma.issue(V, (kt + 1) * BNA, T_, vbuf + ((kt + 1) & 1) * G::BYTES, wave);
     }
-    // Only tiles that reach past the wave's first row need the causal mask.
-    const bool diag = key0 + BN - 1 > row0 || key0 + BN > T_;
-
-    f32x4 s[RB][BN / 16];
+  };
+  for (int kt = 0; kt <= wlast; ++kt) {
+    const int key0 = kt * BNA;
+    const char* kt_lds = kbuf + (kt & 1) * G::BYTES;
+    const char* vt_lds = vbuf + (kt & 1) * G::BYTES;
+    // Every K and V operand of the tile is read into registers before the next tile's
+    // loads are issued: the compiler cannot tell which buffer an in-flight LDS load
+    // writes, and would otherwise wait for it before these reads. The V reads then have
+    // the QK product and the softmax to land.
+    V8 ak[D / 32][BNA / 16];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+    for (int kk = 0; kk < D / 32; ++kk)
 #pragma unroll
-      for (int kb = 0; kb < BN / 16; ++kb) s[rb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) {       // consecutive MFMAs use different accumulators
-      V8 a[BN / 16];
-#pragma unroll
-      for (int kb = 0; kb < BN / 16; ++kb) a[kb] = ld8(k_tile + (kb * 16 + l16) * KS + kk * 32 + 8 * g);
-#pragma unroll
-      for (int kb = 0; kb < BN / 16; ++kb)
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) s[rb][kb] = mfma16x16x32(a[kb], qa[rb][kk], s[rb][kb]);
-    }
-
-    // Online softmax in the log2 domain with the 1/sqrt(d) scale folded into one FMA
-    // per logit. The running max only moves when a row's new max exceeds it by more
-    // than kLazy (checked per wave), so most tiles skip the output rescale; P then
-    // stays <= 2^kLazy, well inside fp16/bf16 range.
-    V8 pb[RB][BN / 32], pl[RB][BN / 32];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int qrow = row0 + rb * 16 + l16;
-      float mx = -INFINITY;
-      if (diag) {
-#pragma unroll
-        for (int kb = 0; kb < BN / 16; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = key0 + kb * 16 + 4 * g + i;
-            if (key > qrow || key >= T_) s[rb][kb][i] = -INFINITY;
-            mx = fmaxf(mx, s[rb][kb][i]);
-          }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < BN / 16; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[rb][kb][i]);
+      for (int kb = 0; kb < BNA / 16; ++kb) {
+        const int row = kb * 16 + l16;
+        ak[kk][kb] = *reinterpret_cast<const V8*>(kt_lds + row * G::ROW + swz_k<G::CPR>(row, kk * 4 + g) * 16);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-      const float mt = mx * p.qk_scale;
-      const bool grow = mt > m[rb] + kLazy;
-      if (__any(grow)) {
-        const float mnew = grow ? mt : m[rb];
-        const float alpha = fast_exp2(m[rb] - mnew);
-        m[rb] = mnew;
-        ls[rb] *= alpha;
+    V8 av[BNA / 32][D / 16];
 #pragma unroll
-        for (int db = 0; db < D / 16; ++db) o[rb][db] *= alpha;
-      }
-      const float nm = -m[rb];
-      float ps = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < BN / 16; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float x = fast_exp2(fmaf(s[rb][kb][i], p.qk_scale, nm));
-          s[rb][kb][i] = x;
-          ps += x;
-        }
-      ls[rb] += ps;
-#pragma unroll
-      for (int ks = 0; ks < BN / 32; ++ks)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pb[rb][ks][i] = (T)s[rb][2 * ks][i];
-          pb[rb][ks][4 + i] = (T)s[rb][2 * ks + 1][i];
-          if constexpr (kSplit) {
-            pl[rb][ks][i] = (T)(s[rb][2 * ks][i] - (float)pb[rb][ks][i]);
-            pl[rb][ks][4 + i] = (T)(s[rb][2 * ks + 1][i] - (float)pb[rb][ks][4 + i]);
-          }
-        }
-    }
-
-#pragma unroll
-    for (int ks = 0; ks < BN / 32; ++ks)
+    for (int ks = 0; ks < BNA / 32; ++ks)
 #pragma unroll
       for (int db = 0; db < D / 16; ++db) {
-        // keys ks*32 + 4g + r (then + 16) of dim db*16 + l16: lane 4r + q of each
-        // 16-lane group points at V[key][db*16 + 4q]
-        const T* vr = v_tile + (ks * 32 + 4 * g + (l16 >> 2)) * VS + db * 16 + 4 * (l16 & 3);
-        const V4 lo = TrRead<T>::read(vr);
-        const V4 hi = TrRead<T>::read(vr + 16 * VS);
-        const V8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        // keys ks*32 + 4g + r (then + 16) of dims db*16 + 4q .. + 3, lane 4r + q of each
+        // 16-lane group; both rows share one swizzle (they differ by 16)
+        const int row = ks * 32 + 4 * g + (l16 >> 2), q = l16 & 3;
+        const char* vr = vt_lds + row * G::ROW + swz_v<G::CPR>(row, 2 * db + (q >> 1)) * 16 + (q & 1) * 8;
+        const V4 lo = TrRead<T>::read(reinterpret_cast<const T*>(vr));
+        const V4 hi = TrRead<T>::read(reinterpret_cast<const T*>(vr + 16 * G::ROW));
+        av[ks][db] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+    prefetch(kt);
+    __builtin_amdgcn_sched_barrier(0);          // reads and loads go out before the math
+    {
+      // Only tiles that reach past the wave's first row (or past T) need the mask.
+      const bool diag = key0 + BNA - 1 > row0 || key0 + BNA > T_;
+      f32x4 s[RB][BNA / 16];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int kb = 0; kb < BNA / 16; ++kb) s[rb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk)       // consecutive MFMAs use different accumulators
+#pragma unroll
+        for (int kb = 0; kb < BNA / 16; ++kb)
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) s[rb][kb] = mfma16x16x32(ak[kk][kb], qa[rb][kk], s[rb][kb]);
+
+      // Online softmax in the log2 domain with the 1/sqrt(d) scale folded into one FMA
+      // per logit. The running max only moves when a row's new max exceeds it by more
+      // than kLazy (checked once per wave for all its rows), so most tiles skip the output
+      // rescale; P then stays <= 2^kLazy, well inside fp16/bf16 range. The row maxima
+      // come first and the exponentials, sums and PV products of all row blocks follow
+      // in one straight stretch, so one block's MFMAs overlap the next block's
+      // exponentials; sums and maxima are pairwise trees (short dependency chains).
+      constexpr int NE = BNA / 16 * 4;            // logits per lane per row block
+      float mt[RB];
+      bool grow = false;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        float e[NE];
+#pragma unroll
+        for (int kb = 0; kb < BNA / 16; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) e[kb * 4 + i] = s[rb][kb][i];
+        if (diag) {
+          const int qrow = row0 + rb * 16 + l16;
+#pragma unroll
+          for (int kb = 0; kb < BNA / 16; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = key0 + kb * 16 + 4 * g + i;
+              if (key > qrow || key >= T_) s[rb][kb][i] = e[kb * 4 + i] = -INFINITY;
+            }
+        }
+#pragma unroll
+        for (int w = NE / 2; w >= 1; w /= 2)
+#pragma unroll
+          for (int j = 0; j < w; ++j) e[j] = fmaxf(e[j], e[j + w]);
+        mt[rb] = quad_row_max(e[0]) * p.qk_scale;
+        grow |= mt[rb] > m[rb] + kLazy;
+      }
+      if (__any(grow)) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-          o[rb][db] = mfma16x16x32(a, pb[rb][ks], o[rb][db]);
-          if constexpr (kSplit) o[rb][db] = mfma16x16x32(a, pl[rb][ks], o[rb][db]);
+          const float mnew = mt[rb] > m[rb] + kLazy ? mt[rb] : m[rb];
+          const float alpha = fast_exp2(m[rb] - mnew);
+          m[rb] = mnew;
+          ls[rb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < D / 16; ++db) o[rb][db] *= alpha;
         }
       }
+      V8 pb[RB][BNA / 32], pl[RB][BNA / 32];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const float nm = -m[rb];
+        float e[NE];
+#pragma unroll
+        for (int kb = 0; kb < BNA / 16; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float x = fast_exp2(fmaf(s[rb][kb][i], p.qk_scale, nm));
+            s[rb][kb][i] = x;
+            e[kb * 4 + i] = x;
+          }
+#pragma unroll
+        for (int w = NE / 2; w >= 1; w /= 2)
+#pragma unroll
+          for (int j = 0; j < w; ++j) e[j] += e[j + w];
+        ls[rb] += e[0];
+#pragma unroll
+        for (int ks = 0; ks < BNA / 32; ++ks)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            pb[rb][ks][i] = (T)s[rb][2 * ks][i];
+            pb[rb][ks][4 + i] = (T)s[rb][2 * ks + 1][i];
+            if constexpr (kSplit) {
+              pl[rb][ks][i] = (T)(s[rb][2 * ks][i] - (float)pb[rb][ks][i]);
+              pl[rb][ks][4 + i] = (T)(s[rb][2 * ks + 1][i] - (float)pb[rb][ks][4 + i]);
+            }
+          }
+      }
+
+#pragma unroll
+      for (int ks = 0; ks < BNA / 32; ++ks)
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            o[rb][db] = mfma16x16x32(av[ks][db], pb[rb][ks], o[rb][db]);
+            if constexpr (kSplit) o[rb][db] = mfma16x16x32(av[ks][db], pl[rb][ks], o[rb][db]);
+          }
+    }
+    __builtin_amdgcn_sched_barrier(0);          // the math stays ahead of the barrier
+    __syncthreads();                            // tile kt + 1 landed; tile kt's buffers free
+  }
+  for (int kt = wlast + 1; kt < nkt; ++kt) {    // tiles past this wave's rows: loads only
+    prefetch(kt);
     __syncthreads();
   }
 
@@ -301,25 +348,51 @@ __global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p)
   }
 }
 
-template <typename T, int D, int RB, bool PREFETCH>
-__global__ __launch_bounds__(kThreads) void prefill_colsum_kernel(PrefillParams p) {
-  using V8 = typename Vec8<T>::type;
-  constexpr int BK = kWaves * 16 * RB;          // keys per workgroup
-  constexpr int KS = Tile<D>::KS;
-  __shared__ __attribute__((aligned(16))) T q_tile[BN * KS];
-  __shared__ float lse_tile[BN];
+// Workgroups are numbered XCD-grouped (see xcd_grid_blocks), so the query blocks of a
+// unit run side by side on one XCD and read its K/V through that XCD's L2.
+template <typename T, int D, int RB>
+__global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p) {
+  constexpr int BM = kWaves * 16 * RB;
+  __shared__ __attribute__((aligned(1024))) char kbuf[2 * DTile<T, D, BNA>::BYTES];
+  __shared__ __attribute__((aligned(1024))) char vbuf[2 * DTile<T, D, BNA>::BYTES];
+  const int nqb = (p.T + BM - 1) / BM;
+  const UnitBlock ub = xcd_unit_block(blockIdx.x, p.units, nqb);
+  if (ub.unit >= p.units) return;
+  attn_block<T, D, RB>(p, ub.unit, nqb - 1 - ub.r, kbuf, vbuf);  // longest first
+}
 
+// Column sums of key block kb (BK keys) of one unit over all query rows at or after it.
+// The wave's keys stay in registers as the A operand; 64-query tiles of Q stream through
+// double-buffered LDS (loaded straight to LDS, one barrier per tile) and each lane keeps
+// the log-sum-exps of its four queries one tile ahead in registers.
+template <typename T, int D, int RB>
+__device__ __forceinline__ void colsum_block(const PrefillParams& p, int unit, int kb, char* qbuf) {
+  using V8 = typename Vec8<T>::type;
+  using G = DTile<T, D, BN>;
+  constexpr int BK = kWaves * 16 * RB;          // keys per workgroup
+  constexpr int QB = BN / 16;                   // 16-query blocks per tile
   const int T_ = p.T;
   const int nq = (T_ + BN - 1) / BN;
-  const int kb = blockIdx.x / p.units;          // early keys (most rows) first
-  const int unit = blockIdx.x - kb * p.units;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
   const size_t base = (size_t)unit * T_ * D;
   const T* Q = static_cast<const T*>(p.q) + base;
   const T* K = static_cast<const T*>(p.k) + base;
   const float* lse = p.lse2 + (size_t)unit * T_;
   const int key0 = kb * BK + wave * 16 * RB;    // this wave's first key
+  const int qt0 = (kb * BK) / BN;
+
+  TileDma<T, D, BN, false> qdma;
+  qdma.init(wave, lane);
+  qdma.issue(Q, qt0 * BN, T_, qbuf, wave);
+  auto load_lse = [&](int q0, float (&l)[QB]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)             // rows past T only meet masked tiles
+      l[qb] = lse[min(q0 + qb * 16 + l16, T_ - 1)];
+  };
+  float lcur[QB], lnext[QB];
+  load_lse(qt0 * BN, lcur);
 
   V8 ka[RB][D / 32];
 #pragma unroll
@@ -337,68 +410,66 @@ __global__ __launch_bounds__(kThreads) void prefill_colsum_kernel(PrefillParams 
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) cs[rb][i] = 0.f;
-
-  const int qt0 = (kb * BK) / BN;
-  RowTile<T, D> qreg;
-  float lreg = 0.f;
-  if constexpr (PREFETCH) {
-    qreg.load(Q, qt0 * BN, T_, tid);
-    if (tid < BN) lreg = qt0 * BN + tid < T_ ? lse[qt0 * BN + tid] : 0.f;
-  }
+  __syncthreads();                              // first tile landed
 
   for (int qt = qt0; qt < nq; ++qt) {
     const int q0 = qt * BN;
-    if constexpr (PREFETCH) {
-      qreg.template store<KS>(q_tile, tid);
-      if (tid < BN) lse_tile[tid] = lreg;
-      __syncthreads();
-      if (qt + 1 < nq) {
-        qreg.load(Q, q0 + BN, T_, tid);
-        if (tid < BN) lreg = q0 + BN + tid < T_ ? lse[q0 + BN + tid] : 0.f;
+    const char* qt_lds = qbuf + ((qt - qt0) & 1) * G::BYTES;
+    // Every operand of the tile is read into registers before the next tile's loads are
+    // issued: the compiler cannot tell which buffer an in-flight LDS load writes, and
+    // would otherwise wait for it before these reads.
+    V8 b[D / 32][QB];
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int row = qb * 16 + l16;
+        b[kk][qb] = *reinterpret_cast<const V8*>(qt_lds + row * G::ROW + swz_k<G::CPR>(row, kk * 4 + g) * 16);
       }
-      __builtin_amdgcn_sched_barrier(0);        // next tile's loads go out first
-    } else {
-      qreg.load(Q, q0, T_, tid);
-      if (tid < BN) lreg = q0 + tid < T_ ? lse[q0 + tid] : 0.f;
-      qreg.template store<KS>(q_tile, tid);
-      if (tid < BN) lse_tile[tid] = lreg;
-      __syncthreads();
+    if (qt + 1 < nq) {                          // its buffer was freed by the last barrier
+      load_lse(q0 + BN, lnext);                 // first: waiting for these leaves the tile loads in flight
+      qdma.issue(Q, q0 + BN, T_, qbuf + ((qt - qt0 + 1) & 1) * G::BYTES, wave);
     }
-    const bool diag = q0 < key0 + 16 * RB;      // some queries of the tile precede some keys
-    f32x4 s[BN / 16][RB];
+    __builtin_amdgcn_sched_barrier(0);          // reads and loads go out before the math
+    // Tile math; MASK for the tiles that reach the diagonal or run past T (a separate
+    // instantiation, so the unmasked tiles carry no selects).
+    auto math = [&](auto mask_c) {
+      constexpr bool MASK = decltype(mask_c)::value;
+      f32x4 s[QB][RB];
 #pragma unroll
-    for (int qb = 0; qb < BN / 16; ++qb)
+      for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) s[qb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int rb = 0; rb < RB; ++rb) s[qb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) {       // consecutive MFMAs use different accumulators
-      V8 b[BN / 16];
+      for (int kk = 0; kk < D / 32; ++kk)       // consecutive MFMAs use different accumulators
 #pragma unroll
-      for (int qb = 0; qb < BN / 16; ++qb) b[qb] = ld8(q_tile + (qb * 16 + l16) * KS + kk * 32 + 8 * g);
+        for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int qb = 0; qb < BN / 16; ++qb)
+          for (int rb = 0; rb < RB; ++rb) s[qb][rb] = mfma16x16x32(ka[rb][kk], b[kk][qb], s[qb][rb]);
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) s[qb][rb] = mfma16x16x32(ka[rb][kk], b[qb], s[qb][rb]);
-    }
-    const bool masked = diag || q0 + BN > T_;
+      for (int qb = 0; qb < QB; ++qb) {
+        const int q = q0 + qb * 16 + l16;
+        const float nl = -lcur[qb];
 #pragma unroll
-    for (int qb = 0; qb < BN / 16; ++qb) {
-      const int q = q0 + qb * 16 + l16;
-      const float nl = -lse_tile[qb * 16 + l16];
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e = fast_exp2(fmaf(s[qb][rb][i], p.qk_scale, nl));
-          if (masked) {
-            const int key = key0 + rb * 16 + 4 * g + i;
-            cs[rb][i] += (q < T_ && q >= key) ? e : 0.f;
-          } else {
-            cs[rb][i] += e;
+          for (int i = 0; i < 4; ++i) {
+            const float e = fast_exp2(fmaf(s[qb][rb][i], p.qk_scale, nl));
+            if constexpr (MASK) {
+              const int key = key0 + rb * 16 + 4 * g + i;
+              cs[rb][i] += (q < T_ && q >= key) ? e : 0.f;
+            } else {
+              cs[rb][i] += e;
+            }
           }
-        }
-    }
-    __syncthreads();
+      }
+    };
+    if (q0 < key0 + 16 * RB || q0 + BN > T_) math(std::true_type{});
+    else math(std::false_type{});
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) lcur[qb] = lnext[qb];
+    __builtin_amdgcn_sched_barrier(0);          // the math stays ahead of the barrier
+    __syncthreads();                            // next tile landed; this tile's buffer free
   }
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
@@ -410,38 +481,40 @@ __global__ __launch_bounds__(kThreads) void prefill_colsum_kernel(PrefillParams 
     }
 }
 
-// Tuning knobs (compile-time): 16-row blocks per wave and register prefetch of the
-// next tile, for the attention and the column-sum kernels.
-// Defaults from a sweep on MI355X (OPT-30B-shaped prompt, T = 2048): attention
-// 2.06 ms with RB = 2 + prefetch vs 3.2 ms with RB = 1; column sums 1.11 ms with
-// RB = 2 and no prefetch.
+// Numbered XCD-grouped like the attention blocks; early keys (the most query rows) first.
+template <typename T, int D, int RB>
+__global__ __launch_bounds__(kThreads) void prefill_colsum_kernel(PrefillParams p) {
+  constexpr int BK = kWaves * 16 * RB;
+  __shared__ __attribute__((aligned(1024))) char qbuf[2 * DTile<T, D, BN>::BYTES];
+  const int nb = (p.T + BK - 1) / BK;
+  const UnitBlock ub = xcd_unit_block(blockIdx.x, p.units, nb);
+  if (ub.unit >= p.units) return;
+  colsum_block<T, D, RB>(p, ub.unit, ub.r, qbuf);
+}
+
+// Tuning knobs (compile-time): 16-row blocks per wave. Defaults from sweeps on MI355X
+// (OPT-30B-shaped prompt, T = 2048).
 #ifndef H2O_ATTN_RB
 #define H2O_ATTN_RB 2
 #endif
-#ifndef H2O_ATTN_PREFETCH
-#define H2O_ATTN_PREFETCH 1
-#endif
 #ifndef H2O_COLSUM_RB
 #define H2O_COLSUM_RB 2
-#endif
-#ifndef H2O_COLSUM_PREFETCH
-#define H2O_COLSUM_PREFETCH 0
 #endif
 
 template <typename T, int D>
 hipError_t attn(const PrefillParams& p, hipStream_t s) {
   constexpr int BM = kWaves * 16 * H2O_ATTN_RB;
   const int nqb = (p.T + BM - 1) / BM;
-  prefill_attn_kernel<T, D, H2O_ATTN_RB, H2O_ATTN_PREFETCH != 0>
-      <<<dim3((unsigned)(nqb * p.units)), dim3(kThreads), 0, s>>>(p);
+  prefill_attn_kernel<T, D, H2O_ATTN_RB>
+      <<<dim3((unsigned)xcd_grid_blocks(p.units, nqb)), dim3(kThreads), 0, s>>>(p);
   return hipGetLastError();
 }
 template <typename T, int D>
 hipError_t colsum(const PrefillParams& p, hipStream_t s) {
   constexpr int BK = kWaves * 16 * H2O_COLSUM_RB;
   const int nb = (p.T + BK - 1) / BK;
-  prefill_colsum_kernel<T, D, H2O_COLSUM_RB, H2O_COLSUM_PREFETCH != 0>
-      <<<dim3((unsigned)(nb * p.units)), dim3(kThreads), 0, s>>>(p);
+  prefill_colsum_kernel<T, D, H2O_COLSUM_RB>
+      <<<dim3((unsigned)xcd_grid_blocks(p.units, nb)), dim3(kThreads), 0, s>>>(p);
   return hipGetLastError();
 }
 

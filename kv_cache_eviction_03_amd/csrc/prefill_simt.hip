@@ -41,9 +41,10 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(PrefillParams p) {
   constexpr int DP = D / 16;
   const int T_ = p.T;
   const int nqb = (T_ + RB - 1) / RB;
-  const int r = blockIdx.x / p.units;
-  const int unit = blockIdx.x - r * p.units;
-  const int qb = nqb - 1 - r;
+  const UnitBlock ub = xcd_unit_block(blockIdx.x, p.units, nqb);
+  if (ub.unit >= p.units) return;
+  const int unit = ub.unit;
+  const int qb = nqb - 1 - ub.r;
   const int qi = threadIdx.x / 16, part = threadIdx.x % 16;
   const int q = qb * RB + qi;
   const int qc = q < T_ ? q : T_ - 1;   // rows past T compute a copy, never stored
@@ -86,8 +87,10 @@ template <int D>
 __global__ __launch_bounds__(kThreads) void colsum_f32_kernel(PrefillParams p) {
   constexpr int DP = D / 16;
   const int T_ = p.T;
-  const int kb = blockIdx.x / p.units;
-  const int unit = blockIdx.x - kb * p.units;
+  const UnitBlock ub = xcd_unit_block(blockIdx.x, p.units, (T_ + RB - 1) / RB);
+  if (ub.unit >= p.units) return;
+  const int unit = ub.unit;
+  const int kb = ub.r;
   const int kj = kb * RB + threadIdx.x / 16, part = threadIdx.x % 16;
   const int kc = kj < T_ ? kj : T_ - 1;
   const size_t base = (size_t)unit * T_ * D;
@@ -111,7 +114,7 @@ __global__ __launch_bounds__(kThreads) void colsum_f32_kernel(PrefillParams p) {
 
 hipError_t launch_prefill_attn_f32(int D, const PrefillParams& p, hipStream_t s) {
   const int nqb = (p.T + RB - 1) / RB;
-  const dim3 grid((unsigned)(nqb * p.units));
+  const dim3 grid((unsigned)xcd_grid_blocks(p.units, nqb));
   if (D == 64) attn_f32_kernel<64><<<grid, dim3(kThreads), 0, s>>>(p);
   else attn_f32_kernel<128><<<grid, dim3(kThreads), 0, s>>>(p);
   return hipGetLastError();
@@ -119,7 +122,7 @@ hipError_t launch_prefill_attn_f32(int D, const PrefillParams& p, hipStream_t s)
 
 hipError_t launch_prefill_colsum_f32(int D, const PrefillParams& p, hipStream_t s) {
   const int nb = (p.T + RB - 1) / RB;
-  const dim3 grid((unsigned)(nb * p.units));
+  const dim3 grid((unsigned)xcd_grid_blocks(p.units, nb));
   if (D == 64) colsum_f32_kernel<64><<<grid, dim3(kThreads), 0, s>>>(p);
   else colsum_f32_kernel<128><<<grid, dim3(kThreads), 0, s>>>(p);
   return hipGetLastError();

@@ -85,6 +85,8 @@ def test_null_descriptor():
     (dict(ws=0), h2o.H2O_ERR_WORKSPACE),
     (dict(ws_bytes=16), h2o.H2O_ERR_WORKSPACE),
     (dict(ws=A + 16), h2o.H2O_ERR_INVALID),
+    # one unit's prompt rows past 2^31 - 1 bytes (2^23 + 1 rows of 128 fp16)
+    (dict(T=2**23 + 1), h2o.H2O_ERR_UNSUPPORTED),
 ])
 def test_prefill_checks(args, status):
     a = dict(q=A, k=A, v=A, T=64, out=A, colsum=0, ws=A, ws_bytes=1 << 20)
