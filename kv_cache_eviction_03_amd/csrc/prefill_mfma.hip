@@ -76,10 +76,7 @@ template <> struct TrRead<__bf16> {
 constexpr int kRsrcWord3 = 0x00020000;   // gfx9 untyped buffer access (32-bit data format)
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
-#ifndef H2O_ATTN_BN
-#define H2O_ATTN_BN 32
-#endif
-constexpr int BNA = H2O_ATTN_BN;   // keys per attention tile
+constexpr int BNA = 32;   // keys per attention tile (one PV MFMA deep)
 
 template <typename T, int D, int ROWS> struct DTile {
   static constexpr int ROW = D * (int)sizeof(T);             // bytes per row
@@ -129,17 +126,24 @@ __device__ __forceinline__ float quad_row_max(float v) {
 }
 
 // Causal attention of query block qb (BM rows) of one unit over all keys up to the block's
-// last row. K and V tiles are double-buffered in LDS (kbuf / vbuf hold two tiles each):
-// the loads of tile kt + 1 are in flight while tile kt is consumed, and one barrier per
-// tile separates the buffer generations.
+// last row, software-pipelined over 32-key tiles. The wave's logits of tile kt come from
+// the previous step; after the row maxima (and the rare output rescale, in its own
+// branch) one straight stretch of code holds the QK product of tile kt + 1, the
+// exponentials, sums and conversions of tile kt, then its PV product, so the matrix unit
+// runs while the vector ALU forms P. K and V tiles are double-buffered in LDS with K one
+// tile ahead of V: in step kt the wave reads K(kt + 1) and V(kt), then starts the loads
+// of K(kt + 2) and V(kt + 1) into the buffers the previous barrier freed.
 template <typename T, int D, int RB>
 __device__ __forceinline__ void attn_block(const PrefillParams& p, int unit, int qb,
-                                           char* kbuf, char* vbuf) {
+                                                char* kbuf, char* vbuf) {
   using V8 = typename Vec8<T>::type;
   using V4 = typename Vec8<T>::half;
   using G = DTile<T, D, BNA>;
   constexpr bool kSplit = !__is_same(T, _Float16);
   constexpr int BM = kWaves * 16 * RB;
+  typedef f32x4 STile[RB][BNA / 16];
+  typedef V8 KOps[D / 32][BNA / 16];
+  typedef V8 VOps[BNA / 32][D / 16];
   const int T_ = p.T;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -158,6 +162,7 @@ __device__ __forceinline__ void attn_block(const PrefillParams& p, int unit, int
   const int nkt = (kend + BNA - 1) / BNA;
   kdma.issue(K, 0, T_, kbuf, wave);
   vdma.issue(V, 0, T_, vbuf, wave);
+  if (nkt > 1) kdma.issue(K, BNA, T_, kbuf + G::BYTES, wave);
 
   V8 qa[RB][D / 32];
 #pragma unroll
@@ -179,34 +184,23 @@ __device__ __forceinline__ void attn_block(const PrefillParams& p, int unit, int
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  // Tiles past this wave's last row are not computed (their loads are still issued).
+  // This wave computes tiles 0..wlast. Its rows start on a tile boundary, so every tile
+  // before wlast lies wholly below the diagonal and below T: only tile wlast is masked.
+  static_assert((16 * RB) % BNA == 0, "a wave's rows must start on a key-tile boundary");
   const int wlast = (min(row0 + 16 * RB, kend) - 1) / BNA;
-  __syncthreads();                              // tile 0 landed
 
-  // Next tile's loads go into the buffers freed by the last barrier.
-  auto prefetch = [&](int kt) {
-    if (kt + 1 < nkt) {
-      kdma.issue(K, (kt + 1) * BNA, T_, kbuf + ((kt + 1) & 1) * G::BYTES, wave);
-      vdma.issue(V, (kt + 1) * BNA, T_, vbuf + ((kt + 1) & 1) * G::BYTES, wave);
-    }
-  };
-  for (int kt = 0; kt <= wlast; ++kt) {
-    const int key0 = kt * BNA;
-    const char* kt_lds = kbuf + (kt & 1) * G::BYTES;
-    const char* vt_lds = vbuf + (kt & 1) * G::BYTES;
-    // Every K and V operand of the tile is read into registers before the next tile's
-    // loads are issued: the compiler cannot tell which buffer an in-flight LDS load
-    // writes, and would otherwise wait for it before these reads. The V reads then have
-    // the QK product and the softmax to land.
-    V8 ak[D / 32][BNA / 16];
+  auto read_k = [&](int kt, KOps& ak) {
+    const char* t = kbuf + (kt & 1) * G::BYTES;
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk)
 #pragma unroll
       for (int kb = 0; kb < BNA / 16; ++kb) {
         const int row = kb * 16 + l16;
-        ak[kk][kb] = *reinterpret_cast<const V8*>(kt_lds + row * G::ROW + swz_k<G::CPR>(row, kk * 4 + g) * 16);
+        ak[kk][kb] = *reinterpret_cast<const V8*>(t + row * G::ROW + swz_k<G::CPR>(row, kk * 4 + g) * 16);
       }
-    V8 av[BNA / 32][D / 16];
+  };
+  auto read_v = [&](int kt, VOps& av) {
+    const char* t = vbuf + (kt & 1) * G::BYTES;
 #pragma unroll
     for (int ks = 0; ks < BNA / 32; ++ks)
 #pragma unroll
@@ -214,119 +208,151 @@ __device__ __forceinline__ void attn_block(const PrefillParams& p, int unit, int
         // keys ks*32 + 4g + r (then + 16) of dims db*16 + 4q .. + 3, lane 4r + q of each
         // 16-lane group; both rows share one swizzle (they differ by 16)
         const int row = ks * 32 + 4 * g + (l16 >> 2), q = l16 & 3;
-        const char* vr = vt_lds + row * G::ROW + swz_v<G::CPR>(row, 2 * db + (q >> 1)) * 16 + (q & 1) * 8;
+        const char* vr = t + row * G::ROW + swz_v<G::CPR>(row, 2 * db + (q >> 1)) * 16 + (q & 1) * 8;
         const V4 lo = TrRead<T>::read(reinterpret_cast<const T*>(vr));
         const V4 hi = TrRead<T>::read(reinterpret_cast<const T*>(vr + 16 * G::ROW));
         av[ks][db] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
-    prefetch(kt);
+  };
+  auto qk = [&](const KOps& ak, STile& s) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int kb = 0; kb < BNA / 16; ++kb) s[rb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk)         // consecutive MFMAs use different accumulators
+#pragma unroll
+      for (int kb = 0; kb < BNA / 16; ++kb)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) s[rb][kb] = mfma16x16x32(ak[kk][kb], qa[rb][kk], s[rb][kb]);
+  };
+  // Start the loads of K(kt + 2) and V(kt + 1).
+  auto loads = [&](int kt) {
+    if (kt + 2 < nkt) kdma.issue(K, (kt + 2) * BNA, T_, kbuf + (kt & 1) * G::BYTES, wave);
+    if (kt + 1 < nkt) vdma.issue(V, (kt + 1) * BNA, T_, vbuf + ((kt + 1) & 1) * G::BYTES, wave);
+  };
+
+  // Tile kt: softmax of s (its logits), PV; with NEXT the QK product of tile kt + 1 into sn.
+  auto tile = [&](auto mask_c, auto next_c, int kt, STile& s, STile& sn) {
+    constexpr bool MASK = decltype(mask_c)::value;
+    constexpr bool NEXT = decltype(next_c)::value;
+    KOps ak;
+    VOps av;
+    if constexpr (NEXT) read_k(kt + 1, ak);
+    read_v(kt, av);
+    loads(kt);
     __builtin_amdgcn_sched_barrier(0);          // reads and loads go out before the math
-    {
-      // Only tiles that reach past the wave's first row (or past T) need the mask.
-      const bool diag = key0 + BNA - 1 > row0 || key0 + BNA > T_;
-      f32x4 s[RB][BNA / 16];
+    const int key0 = kt * BNA;
+    constexpr int NE = BNA / 16 * 4;            // logits per lane per row block
+    float mnew[RB];
+    bool grow = false;
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int kb = 0; kb < BNA / 16; ++kb) s[rb][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk)       // consecutive MFMAs use different accumulators
-#pragma unroll
-        for (int kb = 0; kb < BNA / 16; ++kb)
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) s[rb][kb] = mfma16x16x32(ak[kk][kb], qa[rb][kk], s[rb][kb]);
-
-      // Online softmax in the log2 domain with the 1/sqrt(d) scale folded into one FMA
-      // per logit. The running max only moves when a row's new max exceeds it by more
-      // than kLazy (checked once per wave for all its rows), so most tiles skip the output
-      // rescale; P then stays <= 2^kLazy, well inside fp16/bf16 range. The row maxima
-      // come first and the exponentials, sums and PV products of all row blocks follow
-      // in one straight stretch, so one block's MFMAs overlap the next block's
-      // exponentials; sums and maxima are pairwise trees (short dependency chains).
-      constexpr int NE = BNA / 16 * 4;            // logits per lane per row block
-      float mt[RB];
-      bool grow = false;
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        float e[NE];
-#pragma unroll
-        for (int kb = 0; kb < BNA / 16; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) e[kb * 4 + i] = s[rb][kb][i];
-        if (diag) {
-          const int qrow = row0 + rb * 16 + l16;
-#pragma unroll
-          for (int kb = 0; kb < BNA / 16; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int key = key0 + kb * 16 + 4 * g + i;
-              if (key > qrow || key >= T_) s[rb][kb][i] = e[kb * 4 + i] = -INFINITY;
-            }
-        }
-#pragma unroll
-        for (int w = NE / 2; w >= 1; w /= 2)
-#pragma unroll
-          for (int j = 0; j < w; ++j) e[j] = fmaxf(e[j], e[j + w]);
-        mt[rb] = quad_row_max(e[0]) * p.qk_scale;
-        grow |= mt[rb] > m[rb] + kLazy;
-      }
-      if (__any(grow)) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const float mnew = mt[rb] > m[rb] + kLazy ? mt[rb] : m[rb];
-          const float alpha = fast_exp2(m[rb] - mnew);
-          m[rb] = mnew;
-          ls[rb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < D / 16; ++db) o[rb][db] *= alpha;
-        }
-      }
-      V8 pb[RB][BNA / 32], pl[RB][BNA / 32];
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const float nm = -m[rb];
-        float e[NE];
+    for (int rb = 0; rb < RB; ++rb) {
+      float e[NE];
+      if constexpr (MASK) {
+        const int qrow = row0 + rb * 16 + l16;
 #pragma unroll
         for (int kb = 0; kb < BNA / 16; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float x = fast_exp2(fmaf(s[rb][kb][i], p.qk_scale, nm));
-            s[rb][kb][i] = x;
-            e[kb * 4 + i] = x;
-          }
-#pragma unroll
-        for (int w = NE / 2; w >= 1; w /= 2)
-#pragma unroll
-          for (int j = 0; j < w; ++j) e[j] += e[j + w];
-        ls[rb] += e[0];
-#pragma unroll
-        for (int ks = 0; ks < BNA / 32; ++ks)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            pb[rb][ks][i] = (T)s[rb][2 * ks][i];
-            pb[rb][ks][4 + i] = (T)s[rb][2 * ks + 1][i];
-            if constexpr (kSplit) {
-              pl[rb][ks][i] = (T)(s[rb][2 * ks][i] - (float)pb[rb][ks][i]);
-              pl[rb][ks][4 + i] = (T)(s[rb][2 * ks + 1][i] - (float)pb[rb][ks][4 + i]);
-            }
+            const int key = key0 + kb * 16 + 4 * g + i;
+            if (key > qrow || key >= T_) s[rb][kb][i] = -INFINITY;
           }
       }
-
+#pragma unroll
+      for (int kb = 0; kb < BNA / 16; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) e[kb * 4 + i] = s[rb][kb][i];
+#pragma unroll
+      for (int w = NE / 2; w >= 1; w /= 2)
+#pragma unroll
+        for (int j = 0; j < w; ++j) e[j] = fmaxf(e[j], e[j + w]);
+      const float mt = quad_row_max(e[0]) * p.qk_scale;
+      const bool gr = mt > m[rb] + kLazy;       // the running max moves only by > kLazy
+      mnew[rb] = gr ? mt : m[rb];
+      grow |= gr;
+    }
+    if (__any(grow)) {                          // rare: rescale what was accumulated so far
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const float alpha = fast_exp2(m[rb] - mnew[rb]);
+        m[rb] = mnew[rb];
+        ls[rb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) o[rb][db] *= alpha;
+      }
+    }
+    // One straight stretch from here to the barrier: the next tile's QK MFMAs, this
+    // tile's exponentials and conversions, then its PV MFMAs.
+    if constexpr (NEXT) qk(ak, sn);
+    V8 pb[RB][BNA / 32], pl[RB][BNA / 32];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float nm = -m[rb];
+      float e[NE];
+#pragma unroll
+      for (int kb = 0; kb < BNA / 16; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x = fast_exp2(fmaf(s[rb][kb][i], p.qk_scale, nm));
+          s[rb][kb][i] = x;
+          e[kb * 4 + i] = x;
+        }
+#pragma unroll
+      for (int w = NE / 2; w >= 1; w /= 2)
+#pragma unroll
+        for (int j = 0; j < w; ++j) e[j] += e[j + w];
+      ls[rb] += e[0];
 #pragma unroll
       for (int ks = 0; ks < BNA / 32; ++ks)
 #pragma unroll
-        for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) {
-            o[rb][db] = mfma16x16x32(av[ks][db], pb[rb][ks], o[rb][db]);
-            if constexpr (kSplit) o[rb][db] = mfma16x16x32(av[ks][db], pl[rb][ks], o[rb][db]);
+        for (int i = 0; i < 4; ++i) {
+          pb[rb][ks][i] = (T)s[rb][2 * ks][i];
+          pb[rb][ks][4 + i] = (T)s[rb][2 * ks + 1][i];
+          if constexpr (kSplit) {
+            pl[rb][ks][i] = (T)(s[rb][2 * ks][i] - (float)pb[rb][ks][i]);
+            pl[rb][ks][4 + i] = (T)(s[rb][2 * ks + 1][i] - (float)pb[rb][ks][4 + i]);
           }
+        }
     }
+#pragma unroll
+    for (int ks = 0; ks < BNA / 32; ++ks)
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          o[rb][db] = mfma16x16x32(av[ks][db], pb[rb][ks], o[rb][db]);
+          if constexpr (kSplit) o[rb][db] = mfma16x16x32(av[ks][db], pl[rb][ks], o[rb][db]);
+        }
     __builtin_amdgcn_sched_barrier(0);          // the math stays ahead of the barrier
-    __syncthreads();                            // tile kt + 1 landed; tile kt's buffers free
+    __syncthreads();                            // K(kt + 2), V(kt + 1) landed; old buffers free
+  };
+  using Yes = std::true_type;
+  using No = std::false_type;
+  // Tile kt < wlast: unmasked, and the next tile is this wave's too.
+  auto mid = [&](int kt, STile& s, STile& sn) { tile(No{}, Yes{}, kt, s, sn); };
+
+  STile s0, s1;
+  __syncthreads();                              // K(0), V(0), K(1) landed
+  {
+    KOps ak;
+    read_k(0, ak);
+    qk(ak, s0);
   }
-  for (int kt = wlast + 1; kt < nkt; ++kt) {    // tiles past this wave's rows: loads only
-    prefetch(kt);
+  __syncthreads();                              // K(0) read by every wave: tile 0 reloads its buffer
+  int kt = 0;
+  for (; kt + 1 < wlast; kt += 2) {
+    mid(kt, s0, s1);
+    mid(kt + 1, s1, s0);
+  }
+  if (kt < wlast) {
+    mid(kt, s0, s1);
+    tile(Yes{}, No{}, wlast, s1, s0);           // the wave's last tile reaches the diagonal
+  } else {
+    tile(Yes{}, No{}, wlast, s0, s1);
+  }
+  for (kt = wlast + 1; kt < nkt; ++kt) {        // tiles past this wave's rows: loads only
+    loads(kt);
     __syncthreads();
   }
 
@@ -350,8 +376,10 @@ __device__ __forceinline__ void attn_block(const PrefillParams& p, int unit, int
 
 // Workgroups are numbered XCD-grouped (see xcd_grid_blocks), so the query blocks of a
 // unit run side by side on one XCD and read its K/V through that XCD's L2.
+// Register budget: two waves per SIMD (256 VGPRs), so waves of two workgroups overlap.
 template <typename T, int D, int RB>
-__global__ __launch_bounds__(kThreads) void prefill_attn_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_attn_kernel(PrefillParams p) {
   constexpr int BM = kWaves * 16 * RB;
   __shared__ __attribute__((aligned(1024))) char kbuf[2 * DTile<T, D, BNA>::BYTES];
   __shared__ __attribute__((aligned(1024))) char vbuf[2 * DTile<T, D, BNA>::BYTES];
@@ -440,12 +468,16 @@ __device__ __forceinline__ void colsum_block(const PrefillParams& p, int unit, i
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) s[qb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // Raised issue priority while this wave feeds the matrix unit, so a wave of another
+      // workgroup in its exponential stretch fills the vector ALU meanwhile.
+      __builtin_amdgcn_s_setprio(3);
 #pragma unroll
       for (int kk = 0; kk < D / 32; ++kk)       // consecutive MFMAs use different accumulators
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb) s[qb][rb] = mfma16x16x32(ka[rb][kk], b[kk][qb], s[qb][rb]);
+      __builtin_amdgcn_s_setprio(0);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const int q = q0 + qb * 16 + l16;

@@ -14,7 +14,8 @@
 // how many positions equal to v* must be kept. One ordered ballot sweep over
 // the positions then keeps every candidate above v*, the newest of those equal
 // to v*, and the recent window, writing kept positions to slots in order.
-// Column sums are staged in LDS when they fit (T + k <= 15872 words).
+// Column sums are staged in LDS when they fit (T + k <= 15872 words); the seeded
+// scores are then read back from LDS.
 //
 // reset: slot_pos = -1, acc = 0 (blog §2.3: freeing a slot only marks it).
 #include "h2o_device.hpp"
@@ -61,8 +62,8 @@ __global__ __launch_bounds__(kThreads) void seed_kernel(SeedParams p) {
     for (int s = tid; s < T_; s += kThreads) slot_of[s] = s;
   } else {
     const int ncand = T_ - p.k_local;
-    if (staged)
-      for (int j = tid; j < ncand; j += kThreads) bits[j] = __float_as_uint(c[j]);
+    if (staged)                                 // all T: the seeded scores are read back from here
+      for (int j = tid; j < T_; j += kThreads) bits[j] = __float_as_uint(c[j]);
     auto key = [&](int j) -> unsigned { return staged ? bits[j] : __float_as_uint(c[j]); };
 
     unsigned prefix = 0, mask = 0, want = (unsigned)p.k_heavy, eq_total = 0;
@@ -71,9 +72,26 @@ __global__ __launch_bounds__(kThreads) void seed_kernel(SeedParams p) {
         const int sh = pass * 8;
         hist[tid] = 0;
         __syncthreads();
-        for (int j = tid; j < ncand; j += kThreads) {
-          const unsigned b = key(j);
-          if ((b & mask) == prefix) atomicAdd(&hist[(b >> sh) & 255u], 1u);
+        for (int j0 = 0; j0 < ncand; j0 += kThreads) {
+          const int j = j0 + tid;
+          unsigned bin = 256u;                    // 256: no count from this lane
+          if (j < ncand) {
+            const unsigned b = key(j);
+            if ((b & mask) == prefix) bin = (b >> sh) & 255u;
+          }
+          // Column sums of one prompt share a few exponents, so the high digits pile
+          // into a few bins: the wave counts up to four distinct bins with one ballot
+          // each, and only the lanes left over add one by one.
+          uint64_t pend = __ballot(bin < 256u);
+#pragma unroll
+          for (int it = 0; it < 4 && pend; ++it) {
+            const int leader = __builtin_ctzll(pend);
+            const unsigned lb = (unsigned)__builtin_amdgcn_readlane((int)bin, leader);
+            const uint64_t same = __ballot(bin == lb) & pend;
+            if (lane == leader) atomicAdd(&hist[lb], (unsigned)__popcll(same));
+            pend &= ~same;
+          }
+          if ((pend >> lane) & 1ull) atomicAdd(&hist[bin], 1u);
         }
         __syncthreads();
         // Thread i holds bin 255 - i, so a prefix over threads is a suffix over bins.
@@ -151,7 +169,7 @@ __global__ __launch_bounds__(kThreads) void seed_kernel(SeedParams p) {
     if (s < n_keep) {
       const int j = slot_of[s];
       pos[s] = j;
-      acc[s] = c[j];
+      acc[s] = staged ? __uint_as_float(bits[j]) : c[j];
     } else {
       pos[s] = -1;
       acc[s] = 0.f;
@@ -159,7 +177,7 @@ __global__ __launch_bounds__(kThreads) void seed_kernel(SeedParams p) {
   }
   constexpr int CPR = D * (int)sizeof(T) / 16;   // 16-byte chunks per row
   constexpr int VEC = 16 / (int)sizeof(T);
-  constexpr int B = 4;                           // copies in flight per thread
+  constexpr int B = 4;                           // copies in flight per thread (more measured slower)
   const T* K = static_cast<const T*>(p.k) + (size_t)unit * T_ * D;
   const T* V = static_cast<const T*>(p.v) + (size_t)unit * T_ * D;
   T* ks = static_cast<T*>(p.k_slots) + (size_t)unit * k * D;
