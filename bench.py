@@ -13,10 +13,12 @@ end-to-end token throughput the H2O blog's §3.1.3 defines; the decode-phase
 and prefill-phase rates are reported beside it.
 
 Timing:
-  * timed loop: each step replays two HIP graphs (reset+prefill, then the 32
-    decode launches) with HIP events around each phase, on torch's stream; the
-    decode phase divided by its 32 launches is the decode kernel's mean device
-    duration used for the roofline (it agrees with rocprofv3's kernel trace);
+  * timed loop: each step replays one HIP graph (reset, prefill, the 32 decode
+    launches), with HIP events around the loop, on torch's stream;
+  * phase split: a second loop replays the step as two graphs (reset+prefill, then
+    the 32 decode launches) with HIP events around each phase; the decode phase
+    divided by its 32 launches is the decode kernel's mean device duration used for
+    the roofline (it agrees with rocprofv3's kernel trace);
   * graph replays are checked bit for bit against an eager run;
   * cpu_baseline: the CPU oracle on the same inputs (all 256 units of one step);
   * prefill_mfma_opt30b: the prefill of the OPT-30B-shaped layer (T = 2048), where
@@ -264,10 +266,14 @@ def main():
     ref_state = {k: v.clone() for k, v in cache.state().items() if torch.is_tensor(v)}
     ref_outs = outs.clone()
 
-    # Capture the two phases as HIP graphs.
+    # Capture the whole step as one HIP graph (the timed loop), and each phase as a graph
+    # of its own (a second loop, for the phase split and the decode kernel's duration).
     side = torch.cuda.Stream(dev)
-    g_pre, g_dec = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    g_step, g_pre, g_dec = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
     with torch.cuda.stream(side):
+        with torch.cuda.graph(g_step, stream=side):
+            run_prefill()
+            run_decode()
         with torch.cuda.graph(g_pre, stream=side):
             run_prefill()
         cache.t = T
@@ -277,37 +283,49 @@ def main():
 
     stream = torch.cuda.current_stream(dev)
     for _ in range(args.warmup):
-        g_pre.replay()
-        g_dec.replay()
+        g_step.replay()
     torch.cuda.synchronize()
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # Timed loop: exactly `steps` replays of the whole step.
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
+    for _ in range(args.steps):
+        g_step.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+
+    # Graph replays must reproduce the eager run bit for bit.
+    def check_replay(what):
+        for k, v in ref_state.items():
+            if not torch.equal(getattr(cache, k), v):
+                raise RuntimeError(f"{what} replay diverged from the eager run in {k}")
+        if not torch.equal(outs, ref_outs):
+            raise RuntimeError(f"{what} replay diverged from the eager run in decode outputs")
+    check_replay("step graph")
+
+    # Phase split: the same step as two graphs with events between them.
+    for _ in range(args.warmup):
+        g_pre.replay()
+        g_dec.replay()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
     for e0, e1, e2 in ev:
         e0.record(stream)
         g_pre.replay()
         e1.record(stream)
         g_dec.replay()
         e2.record(stream)
-    end.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall
-    total_ms = start.elapsed_time(end)
     pre_ms = sum(a.elapsed_time(b) for a, b, _ in ev) / args.steps
     dec_ms = sum(b.elapsed_time(c) for _, b, c in ev) / args.steps
-    ms_per_step = total_ms / args.steps
-
-    # Graph replays must reproduce the eager run bit for bit.
-    for k, v in ref_state.items():
-        if not torch.equal(getattr(cache, k), v):
-            raise RuntimeError(f"graph replay diverged from the eager run in {k}")
-    if not torch.equal(outs, ref_outs):
-        raise RuntimeError("graph replay diverged from the eager run in decode outputs")
+    check_replay("phase graph")
 
     # Decode phase = n back-to-back decode launches inside one graph: its mean per launch is
     # the decode kernel's device duration (inter-node gaps included, so conservative).
@@ -338,7 +356,7 @@ def main():
         "config": {
             "workload": f"{w.name}: batch {B}, {H} heads, head_dim {d}, fp16 K/V, prompt {T} + "
                         f"{n} generated, k = {w.k_heavy} heavy + {w.k_local} local slots",
-            "step": f"reset + prefill ({T} tokens) + {n} decode steps, replayed as HIP graphs",
+            "step": f"reset + prefill ({T} tokens) + {n} decode steps, replayed as one HIP graph",
             "value_is": "generated tokens / step time (prefill + decode)",
             "global_batch": B, "seq_len": T + n, "parallelism": "single GPU",
         },
