@@ -143,6 +143,7 @@ __global__ __launch_bounds__(THREADS) void decode_resident_kernel(DecodeParams p
   __shared__ float s_m[ROWS], s_l[ROWS];
   __shared__ float s_logit[ROWS * U];
   __shared__ uint64_t s_key[S::WAVES];
+  __shared__ float s_scw[S::WAVES][ROWS];       // each wave's copy of the scale factors
 
   const int unit = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -184,8 +185,8 @@ __global__ __launch_bounds__(THREADS) void decode_resident_kernel(DecodeParams p
   }
   __syncthreads();                              // (1) every K/V read is consumed
   // Scale factors 2^(m_g - M) of the row groups, formed by every wave for itself with
-  // wave-uniform folds: lane r holds group r (and r + 64), one exp2 per lane, and the
-  // factors reach the output loop as scalars through readlane.
+  // wave-uniform folds (lane r holds group r and r + 64, one exp2 per lane) into the
+  // wave's own LDS copy, so no further barrier is needed.
   static_assert(ROWS <= 2 * kWave, "at most two row groups per lane");
   const float m_a = lane < ROWS ? s_m[lane] : -INFINITY;
   const float m_b = lane + kWave < ROWS ? s_m[lane + kWave] : -INFINITY;
@@ -196,16 +197,24 @@ __global__ __launch_bounds__(THREADS) void decode_resident_kernel(DecodeParams p
                      (lane + kWave < ROWS ? s_l[lane + kWave] * sc_b : 0.f);
   const float inv = __builtin_amdgcn_rcpf(wave_sum_uniform(l_ab));
   const float p_new = fast_exp2(s_logit[n] - M) * inv;
+  if (lane < ROWS) s_scw[wave][lane] = sc_a;
+  if (lane + kWave < ROWS) s_scw[wave][lane + kWave] = sc_b;
 
-  for (int c = tid; c < D; c += THREADS) {
+  // Output: every wave takes CW columns; the SL lanes of one column (lanes c, c + CW, ...)
+  // each sum RS of the row groups, then fold their partial sums with lane swaps.
+  {
+    constexpr int SL = THREADS / D, CW = kWave / SL, RS = ROWS / SL;
+    static_assert(SL * CW == kWave && RS * SL == ROWS, "output split");
+    const int c = wave * CW + lane % CW, sl = lane / CW;
     float v = 0.f;
 #pragma unroll
-    for (int r = 0; r < ROWS; ++r) {
-      const float scr = __uint_as_float(__builtin_amdgcn_readlane(
-          (int)__float_as_uint(r < kWave ? sc_a : sc_b), r % kWave));
-      v = fmaf(s_red[r * D + c], scr, v);
+    for (int j = 0; j < RS; ++j) {
+      const int r = sl * RS + j;
+      v = fmaf(s_red[r * D + c], s_scw[wave][r], v);
     }
-    p.out[(size_t)unit * D + c] = v * inv;
+#pragma unroll
+    for (int w = CW; w < kWave; w *= 2) v += __shfl_xor(v, w, kWave);
+    if (sl == 0) p.out[(size_t)unit * D + c] = v * inv;
   }
 
   uint64_t key = ~0ull;
