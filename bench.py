@@ -24,7 +24,11 @@ Timing:
   * prefill_mfma_opt30b: the prefill of the OPT-30B-shaped layer (T = 2048), where
     prefill is MFMA-bound, against the 2.5 PFLOP/s dense fp16 peak;
   * decode_by_workload: the decode kernel at each workload's layer shape (the
-    LLaMA-7B layer, the OPT-30B layer, the 4096-slot stream), graph-replayed.
+    LLaMA-7B layer, the OPT-30B layer, the 4096-slot stream), graph-replayed;
+  * roofline_cold: the bench workload's decode launch with the 256 MB Infinity Cache
+    out of play (36 replicas of the cache state visited in turn, 519 MB per sweep);
+  * dense_comparator: context only, the same decode steps with k = T + n (nothing
+    evicted) against the H2O budget.
 """
 from __future__ import annotations
 
@@ -172,6 +176,103 @@ def decode_by_workload(ids=(2, 3, 4, 5), n=32, reps=5):
     return res
 
 
+def decode_cold(w, replicas=36, reps=5):
+    """The decode kernel of the bench workload with the Infinity Cache (MALL) out of play.
+
+    `replicas` independent caches, each prefilled from the same prompt, are visited in turn
+    by one graph of `replicas` decode launches, so consecutive launches touch disjoint slot
+    arrays and the state swept per replay (replicas x 14.4 MB > 512 MB) is twice the 256 MB
+    MALL. The same launch shape as the warm figure; best and median replay, per launch.
+    Replays repeat each replica's position t; that leaves the work per launch unchanged.
+    """
+    import statistics
+
+    import torch
+
+    from kv_cache_eviction_03_amd import H2OCache
+    from workloads import generate
+    dev = "cuda:0"
+    x = generate(w, seed=0, device=dev)
+    caches = []
+    for _ in range(replicas):
+        c = H2OCache(w.batch, w.heads, w.head_dim, w.k_heavy, w.k_local, w.torch_dtype, dev,
+                     max_prompt=w.prompt)
+        c.reset()
+        c.prefill(x["q_prompt"], x["k_prompt"], x["v_prompt"])
+        caches.append(c)
+    out = torch.empty((w.batch, w.heads, w.head_dim), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for c in caches:
+                c.decode(x["q_dec"][0], x["k_dec"][0], x["v_dec"][0], out=out)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        per.append(1e3 * a.elapsed_time(b) / replicas)
+    byt = decode_bytes_per_unit(w) * w.units_per_layer
+    best, med = min(per), statistics.median(per)
+    del x, caches, out, g
+    torch.cuda.empty_cache()
+    return {"bound": "hbm", "kernel": "decode_resident_kernel<_Float16,128,256>, MALL-cold",
+            "achieved": byt / (med * 1e-6) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": byt / (med * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "avg_launch_us": med, "best_launch_us": best,
+            "algorithmic_bytes_per_launch": byt, "replicas": replicas,
+            "state_swept_MB": replicas * byt / 1e6,
+            "duration_from": "HIP events around graph replays of one launch per replica (median)"}
+
+
+def dense_comparator(w, reps=5):
+    """Context, not a target: the same decode steps with k = T + n, so nothing is evicted
+    (every prompt and generated token stays cached), against the H2O budget k."""
+    import torch
+
+    from kv_cache_eviction_03_amd import H2OCache
+    from workloads import generate
+    dev = "cuda:0"
+    n = w.steps
+    kd = w.prompt + n
+    x = generate(w, seed=0, device=dev)
+    c = H2OCache(w.batch, w.heads, w.head_dim, kd - w.k_local, w.k_local, w.torch_dtype, dev,
+                 max_prompt=w.prompt)
+    out = torch.empty((n, w.batch, w.heads, w.head_dim), dtype=torch.float32, device=dev)
+    c.reset()
+    c.prefill(x["q_prompt"], x["k_prompt"], x["v_prompt"])
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for i in range(n):
+                c.decode(x["q_dec"][i], x["k_dec"][i], x["v_dec"][i], out=out[i])
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(reps):
+        c.reset()
+        c.prefill(x["q_prompt"], x["k_prompt"], x["v_prompt"])
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        us = 1e3 * a.elapsed_time(b) / n
+        best = us if best is None else min(best, us)
+    del x, c, out, g
+    torch.cuda.empty_cache()
+    return {"workload": f"{w.name} layer with k = T + n = {kd} (no eviction)",
+            "decode_us_per_step": best, "decode_tokens_per_s": w.batch / (best * 1e-6)}
+
+
 def cpu_baseline(w, x, units, min_seconds=10.0):
     import numpy as np
     from threadpoolctl import threadpool_info
@@ -211,6 +312,10 @@ def main():
     ap.add_argument("--decode-shapes", action="store_true",
                     help="only time the decode kernel at each workload's layer shape")
     ap.add_argument("--no-decode-shapes", action="store_true")
+    ap.add_argument("--decode-cold", action="store_true",
+                    help="only time the bench workload's decode kernel with the MALL out of play")
+    ap.add_argument("--no-cold", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 512 MiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -240,6 +345,9 @@ def main():
     from workloads import WORKLOADS, generate
 
     w = WORKLOADS[2]
+    if args.decode_cold:
+        print(json.dumps(decode_cold(w)), flush=True)
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     x = generate(w, seed=args.seed, device=dev)
@@ -386,6 +494,12 @@ def main():
         result["prefill_mfma_opt30b"] = prefill_mfma_probe()
     if not args.no_decode_shapes:
         result["decode_by_workload"] = decode_by_workload()
+    if not args.no_cold:
+        result["roofline_cold"] = decode_cold(w)
+    if not args.no_dense:
+        dense = dense_comparator(w)
+        dense["h2o_decode_speedup"] = dense["decode_us_per_step"] / dec_kernel_us
+        result["dense_comparator"] = dense
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, x, list(range(units)))
     print(json.dumps(result), flush=True)
