@@ -28,7 +28,8 @@ Timing:
   * roofline_cold: the bench workload's decode launch with the 256 MB Infinity Cache
     out of play (36 replicas of the cache state visited in turn, 519 MB per sweep);
   * dense_comparator: context only, the same decode steps with k = T + n (nothing
-    evicted) against the H2O budget.
+    evicted) against the H2O budget;
+  * hbm_measured_ceiling: context only, plain PyTorch streaming read and copy rates.
 """
 from __future__ import annotations
 
@@ -177,13 +178,13 @@ def decode_by_workload(ids=(2, 3, 4, 5), n=32, reps=5):
 
 
 def decode_cold(w, replicas=36, reps=5):
-    """The decode kernel of the bench workload with the Infinity Cache (MALL) out of play.
+    """A workload's decode step with the Infinity Cache (MALL) out of play.
 
     `replicas` independent caches, each prefilled from the same prompt, are visited in turn
-    by one graph of `replicas` decode launches, so consecutive launches touch disjoint slot
-    arrays and the state swept per replay (replicas x 14.4 MB > 512 MB) is twice the 256 MB
-    MALL. The same launch shape as the warm figure; best and median replay, per launch.
-    Replays repeat each replica's position t; that leaves the work per launch unchanged.
+    by one graph of `replicas` decode steps, so consecutive steps touch disjoint slot arrays
+    and the state swept per replay (replicas x the step's bytes, >= 512 MB) is at least twice
+    the 256 MB MALL. The same launch shape as the warm figure; best and median replay, per
+    step. Replays repeat each replica's position t; that leaves the work per step unchanged.
     """
     import statistics
 
@@ -223,13 +224,57 @@ def decode_cold(w, replicas=36, reps=5):
     best, med = min(per), statistics.median(per)
     del x, caches, out, g
     torch.cuda.empty_cache()
-    return {"bound": "hbm", "kernel": "decode_resident_kernel<_Float16,128,256>, MALL-cold",
+    return {"workload": f"{w.name} layer: B {w.batch}, H {w.heads}, d {w.head_dim}, {w.dtype}, "
+                        f"k = {w.k_heavy}+{w.k_local}",
+            "bound": "hbm", "kernel": "decode step, MALL-cold",
             "achieved": byt / (med * 1e-6) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": byt / (med * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "avg_launch_us": med, "best_launch_us": best,
             "algorithmic_bytes_per_launch": byt, "replicas": replicas,
             "state_swept_MB": replicas * byt / 1e6,
             "duration_from": "HIP events around graph replays of one launch per replica (median)"}
+
+
+def hbm_ceiling(reps=10):
+    """Context: what plain PyTorch streaming kernels reach on this HBM (MALL-cold sizes):
+    a 1 GiB fp32 sum (read) and a 512 MiB copy (read + write). Median of `reps`."""
+    import statistics
+
+    import torch
+    n = (1 << 30) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    y = torch.empty(n // 2, dtype=torch.float32, device="cuda:0")
+    out = {}
+    for name, fn, nbytes in (("read_GBps", lambda: x.sum(), 4 * n),
+                             ("copy_GBps", lambda: y.copy_(x[: n // 2]), 4 * n)):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        out[name] = nbytes / statistics.median(ts) / 1e9
+    del x, y
+    torch.cuda.empty_cache()
+    out["note"] = "torch sum over 1 GiB fp32; torch copy of 512 MiB (1 GiB moved); medians"
+    return out
+
+
+def decode_cold_by_workload(ids_replicas=((3, 5), (4, 3), (5, 8))):
+    """MALL-cold decode at the other workloads' layer shapes (cache filled by a k + 64 prompt,
+    so every step evicts)."""
+    from workloads import WORKLOADS
+    res = []
+    for wid, r in ids_replicas:
+        w = WORKLOADS[wid].scaled(prompt=WORKLOADS[wid].k + 64, steps=1, layers=1)
+        d = decode_cold(w, replicas=r)
+        res.append({k: d[k] for k in ("workload", "avg_launch_us", "best_launch_us", "achieved",
+                                      "frac", "replicas", "state_swept_MB")})
+    return res
 
 
 def dense_comparator(w, reps=5):
@@ -347,6 +392,8 @@ def main():
     w = WORKLOADS[2]
     if args.decode_cold:
         print(json.dumps(decode_cold(w)), flush=True)
+        for r in decode_cold_by_workload():
+            print(json.dumps(r), flush=True)
         return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -495,7 +542,11 @@ def main():
     if not args.no_decode_shapes:
         result["decode_by_workload"] = decode_by_workload()
     if not args.no_cold:
+        result["hbm_measured_ceiling"] = hbm_ceiling()
         result["roofline_cold"] = decode_cold(w)
+        result["roofline_cold"]["kernel"] = "decode_resident_kernel<_Float16,128,256>, MALL-cold"
+        if not args.no_decode_shapes:
+            result["decode_cold_by_workload"] = decode_cold_by_workload()
     if not args.no_dense:
         dense = dense_comparator(w)
         dense["h2o_decode_speedup"] = dense["decode_us_per_step"] / dec_kernel_us
