@@ -319,31 +319,41 @@ def dense_comparator(w, reps=5):
 
 
 def cpu_baseline(w, x, units, min_seconds=10.0):
-    import numpy as np
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import run_unit
     host = {k: v.double().cpu().numpy() for k, v in x.items()}
-    # Whole passes over the sampled units until about 10 s of CPU work has been timed.
-    t0 = time.perf_counter()
-    passes = 0
-    while True:
-        for uidx in units:
-            b, h = divmod(uidx, w.heads)
-            run_unit(w.k_heavy, w.k_local, host["q_prompt"][b, h], host["k_prompt"][b, h],
-                     host["v_prompt"][b, h], host["q_dec"][:, b, h], host["k_dec"][:, b, h],
-                     host["v_dec"][:, b, h])
-        passes += 1
-        dt = time.perf_counter() - t0
-        if dt >= min_seconds or passes >= 50:
-            break
-    per_unit = dt / (passes * len(units))
+
+    def timed(min_s, unit_list):
+        # Whole passes over the sampled units until about min_s of CPU work has been timed.
+        t0 = time.perf_counter()
+        passes = 0
+        while True:
+            for uidx in unit_list:
+                b, h = divmod(uidx, w.heads)
+                run_unit(w.k_heavy, w.k_local, host["q_prompt"][b, h], host["k_prompt"][b, h],
+                         host["v_prompt"][b, h], host["q_dec"][:, b, h], host["k_dec"][:, b, h],
+                         host["v_dec"][:, b, h])
+            passes += 1
+            dt = time.perf_counter() - t0
+            if dt >= min_s or passes >= 50:
+                return dt, passes
+
+    def rate(dt, passes, n_units):
+        return w.batch * w.steps / (dt / (passes * n_units) * w.units_per_layer)
+
+    dt, passes = timed(min_seconds, units)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    tokens_per_s = w.batch * w.steps / (per_unit * w.units_per_layer)
-    del np
-    return {"value": tokens_per_s, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    with threadpool_limits(limits=1):           # the same oracle on one core
+        few = units[: max(1, len(units) // 8)]
+        dt1, passes1 = timed(min_seconds / 2, few)
+    return {"value": rate(dt, passes, len(units)), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
             "sample": f"{passes} pass(es) over {len(units)} of {w.units_per_layer} units (prefill + "
-                      f"{w.steps} decode steps each) in {dt:.1f} s, scaled to the whole step"}
+                      f"{w.steps} decode steps each) in {dt:.1f} s, scaled to the whole step",
+            "value_1_core": rate(dt1, passes1, len(few)),
+            "sample_1_core": f"{passes1} pass(es) over {len(few)} units in {dt1:.1f} s, one BLAS "
+                             f"thread, scaled to the whole step"}
 
 
 def main():
