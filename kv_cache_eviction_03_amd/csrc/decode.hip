@@ -327,14 +327,22 @@ __global__ __launch_bounds__(kPartThreads) void decode_split_partial_kernel(Deco
   }
 }
 
+// One memory round trip: the first batch of every load the unit needs (the partial
+// statistics, which every wave folds for itself; the partial outs; the slots' logits,
+// scores and positions; the new token's logit and K/V) is issued before any is
+// consumed. Further batches (more than QB * G splits or R * kCombThreads slots) follow
+// in loops.
 template <typename T, int D>
 __global__ __launch_bounds__(kCombThreads) void decode_split_combine_kernel(DecodeParams p,
                                                                             SplitScratch w) {
   constexpr int VEC = Chunk<T>::N, LANES = D / VEC;
   constexpr int WAVES = kCombThreads / kWave;
   constexpr int G = kCombThreads / D;           // groups that share the partial-out sums
+  constexpr int QB = 8;                         // partial outs per thread per load batch
   constexpr int R = 4;                          // slots per thread per load batch
-  __shared__ float s_ml[2 * kMaxSplits], s_sc[kMaxSplits], s_stat[2];
+  constexpr int MQ = (kMaxSplits + kWave - 1) / kWave;   // partial statistics per lane
+  static_assert(QB * G <= kMaxSplits, "first batch of partial outs");
+  __shared__ float s_scw[WAVES][kMaxSplits];    // each wave's copy of the split scale factors
   __shared__ float s_o[G * D];
   __shared__ uint64_t s_key[WAVES];
   __shared__ int s_dst;
@@ -352,40 +360,78 @@ __global__ __launch_bounds__(kCombThreads) void decode_split_combine_kernel(Deco
   int32_t* pos = p.slot_pos + (size_t)unit * k;
   float* acc = p.acc + (size_t)unit * k;
   const float* logit = w.logits + (size_t)unit * (k + 1);
+  const float* pml = w.part_ml + (size_t)unit * nsplit * 2;
+  const float* po = w.part_o + (size_t)unit * nsplit * D;
+  const int c = tid % D, grp = tid / D;
 
-  if (tid < 2 * nsplit) s_ml[tid] = w.part_ml[(size_t)unit * nsplit * 2 + tid];
-  if (tid == 0) s_dst = full ? -1 : n;
-  __syncthreads();
-  if (tid < kWave) {
-    float m = -INFINITY;
-    for (int q = tid; q < nsplit; q += kWave) m = fmaxf(m, s_ml[2 * q]);
-    m = group_max<kWave>(m);
-    float l = 0.f;
-    for (int q = tid; q < nsplit; q += kWave) {
-      const float sc = s_ml[2 * q] == -INFINITY ? 0.f : fast_exp2(s_ml[2 * q] - m);
-      s_sc[q] = sc;
-      l = fmaf(s_ml[2 * q + 1], sc, l);
-    }
-    l = group_sum<kWave>(l);
-    if (tid == 0) { s_stat[0] = m; s_stat[1] = 1.0f / l; }
+  float pm[MQ], pl[MQ];
+#pragma unroll
+  for (int i = 0; i < MQ; ++i) {
+    const int q = lane + i * kWave, qc = q < nsplit ? q : 0;
+    pm[i] = pml[2 * qc];
+    pl[i] = pml[2 * qc + 1];
   }
-  __syncthreads();
-  const float M = s_stat[0], inv = s_stat[1];
+  float pov[QB];
+#pragma unroll
+  for (int i = 0; i < QB; ++i) {
+    const int q = grp + i * G;
+    pov[i] = po[(size_t)(q < nsplit ? q : 0) * D + c];
+  }
+  float lg[R], ac[R];
+  int ps[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int j = i * kCombThreads + tid, jc = j < n ? j : 0;
+    lg[i] = logit[jc];
+    ac[i] = acc[jc];
+    ps[i] = pos[jc];
+  }
+  const float lg_new = logit[n];
+  const uint4 kvn = ld16((tid < LANES ? kn : vn) + (tid % LANES) * VEC);
+  if (tid == 0) s_dst = full ? -1 : n;
+  __builtin_amdgcn_sched_barrier(0);            // keep every load ahead of the math
+
+  // Global max M and 1 / sum over the splits, wave-uniform in every wave.
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < MQ; ++i)
+    if (lane + i * kWave < nsplit) mx = fmaxf(mx, pm[i]);
+  const float M = wave_max_uniform(mx);
+  float l = 0.f;
+#pragma unroll
+  for (int i = 0; i < MQ; ++i) {
+    const int q = lane + i * kWave;
+    const float sc = q < nsplit && pm[i] != -INFINITY ? fast_exp2(pm[i] - M) : 0.f;
+    if (q < kMaxSplits) s_scw[wave][q] = sc;
+    l = fmaf(pl[i], sc, l);
+  }
+  const float inv = 1.0f / wave_sum_uniform(l);
 
   // out: G groups of D threads each sum every G-th partial, then a fixed-order merge.
   {
-    const int c = tid % D, grp = tid / D;
     float v = 0.f;
-    for (int q = grp; q < nsplit; q += G)
-      v = fmaf(w.part_o[((size_t)unit * nsplit + q) * D + c], s_sc[q], v);
+#pragma unroll
+    for (int i = 0; i < QB; ++i) v = fmaf(pov[i], s_scw[wave][grp + i * G], v);
+    for (int q = grp + QB * G; q < nsplit; q += G)
+      v = fmaf(po[(size_t)q * D + c], s_scw[wave][q], v);
     s_o[grp * D + c] = v;
   }
-  // scores: slots j = tid + i * kCombThreads, R loads of each kind in flight
+  // scores: slot j = tid + i * kCombThreads
   uint64_t best = ~0ull;
   int best_slot = -1;
-  for (int base = 0; base < n; base += R * kCombThreads) {
-    float lg[R], ac[R];
-    int ps[R];
+  auto score = [&](int j, float lgv, float acv, int psv) {
+    if (j < n) {
+      const float a = acv + fast_exp2(lgv - M) * inv;
+      acc[j] = a;
+      if (full && psv <= limit) {
+        const uint64_t key = score_key(a, psv);
+        if (key < best) { best = key; best_slot = j; }
+      }
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < R; ++i) score(i * kCombThreads + tid, lg[i], ac[i], ps[i]);
+  for (int base = R * kCombThreads; base < n; base += R * kCombThreads) {
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       const int j = base + i * kCombThreads + tid, jc = j < n ? j : 0;
@@ -394,17 +440,7 @@ __global__ __launch_bounds__(kCombThreads) void decode_split_combine_kernel(Deco
       ps[i] = pos[jc];
     }
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const int j = base + i * kCombThreads + tid;
-      if (j < n) {
-        const float a = ac[i] + fast_exp2(lg[i] - M) * inv;
-        acc[j] = a;
-        if (full && ps[i] <= limit) {
-          const uint64_t key = score_key(a, ps[i]);
-          if (key < best) { best = key; best_slot = j; }
-        }
-      }
-    }
+    for (int i = 0; i < R; ++i) score(base + i * kCombThreads + tid, lg[i], ac[i], ps[i]);
   }
   const uint64_t wmin = wave_min_u64(best);
   if (lane == 0) s_key[wave] = wmin;
@@ -412,7 +448,7 @@ __global__ __launch_bounds__(kCombThreads) void decode_split_combine_kernel(Deco
   if (tid < D) {
     float v = 0.f;
 #pragma unroll
-    for (int grp = 0; grp < G; ++grp) v += s_o[grp * D + tid];
+    for (int gi = 0; gi < G; ++gi) v += s_o[gi * D + tid];
     p.out[(size_t)unit * D + tid] = v * inv;
   }
   uint64_t gbest = s_key[0];
@@ -423,13 +459,11 @@ __global__ __launch_bounds__(kCombThreads) void decode_split_combine_kernel(Deco
   if (full && best_slot >= 0 && best == gbest) s_dst = best_slot;
   __syncthreads();
   const int dst = s_dst;
-  const float p_new = fast_exp2(logit[n] - M) * inv;
   if (dst >= 0) {
-    if (tid < LANES) st16(ks + (size_t)dst * D + tid * VEC, ld16(kn + tid * VEC));
-    else if (tid < 2 * LANES) st16(vs + (size_t)dst * D + (tid - LANES) * VEC, ld16(vn + (tid - LANES) * VEC));
+    if (tid < 2 * LANES) st16((tid < LANES ? ks : vs) + (size_t)dst * D + (tid % LANES) * VEC, kvn);
     if (tid == dst % kCombThreads) {            // visited slot dst in the score loop
       pos[dst] = t;
-      acc[dst] = p_new;
+      acc[dst] = fast_exp2(lg_new - M) * inv;
     }
   }
   if (tid == 0) {
