@@ -543,7 +543,7 @@ def main():
             "mfma_frac": pre_tflops / MFMA_F16_PEAK_TFLOPS,
             "achieved_gbs": pre_gbs, "hbm_frac": pre_gbs / HBM_PEAK_GBS,
             "avg_phase_us": pre_call_us,
-            "note": "prefill phase = reset + attention + column-sum + seed kernels",
+            "note": "prefill phase = reset + attention-with-column-sums + seed kernels",
         },
         "wall_s_timed_loop": wall,
     }

@@ -120,8 +120,11 @@ h2o_status h2o_reset(const h2o_cache_desc* cache, void* stream);
  *
  * Workspace contract: 256-byte aligned device memory owned by the caller. It is
  * scratch: its contents on entry are ignored and on return are unspecified
- * (prefill keeps row log-sum-exps there; a decode that spreads a unit's slots
- * over several workgroups keeps per-workgroup partials there). One workspace
+ * (prefill keeps per-query-block partial column sums there, about T^2 / 256
+ * floats per unit for fp16/bf16, and the column sums when colsum_out is NULL;
+ * a decode that spreads a unit's slots over several workgroups keeps
+ * per-workgroup partials there). The size grows with max_prompt, so a
+ * workspace sized for max_prompt serves every shorter prompt. One workspace
  * must not be used by two calls that can run at the same time.
  */
 size_t h2o_workspace_bytes(const h2o_cache_desc* cache, int32_t max_prompt);

@@ -53,20 +53,14 @@ template <typename T, int D, int THREADS = 256> struct Shape {
   static constexpr int WAVES = THREADS / kWave;
 };
 
-// DPP lane move inside a 16-lane row (all lanes active).
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
-}
-
 // Sum over each group of WIDTH consecutive lanes; every lane gets the group's sum
 // (the pairings are symmetric, so all lanes of a group hold the same bits).
 template <int WIDTH>
 __device__ __forceinline__ float row_sum(float v) {
-  v += dpp<0xb1>(v);                                    // quad_perm [1,0,3,2]
-  v += dpp<0x4e>(v);                                    // quad_perm [2,3,0,1]
-  if constexpr (WIDTH >= 8) v += dpp<0x141>(v);         // row_half_mirror
-  if constexpr (WIDTH >= 16) v += dpp<0x140>(v);        // row_mirror
+  v += dpp_mov<0xb1>(v);                                    // quad_perm [1,0,3,2]
+  v += dpp_mov<0x4e>(v);                                    // quad_perm [2,3,0,1]
+  if constexpr (WIDTH >= 8) v += dpp_mov<0x141>(v);         // row_half_mirror
+  if constexpr (WIDTH >= 16) v += dpp_mov<0x140>(v);        // row_mirror
   if constexpr (WIDTH >= 32) v += __shfl_xor(v, 16, kWave);
   return v;
 }

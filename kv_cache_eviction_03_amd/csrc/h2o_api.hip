@@ -67,12 +67,28 @@ h2o_status check_desc(const h2o_cache_desc* c) {
 int units_of(const h2o_cache_desc* c) { return c->batch * c->heads; }
 int slots_of(const h2o_cache_desc* c) { return c->k_heavy + c->k_local; }
 
-// Workspace: scratch shared by prefill (log-sum-exp + column sums) and the split decode
-// (per-split partials and logits); its contents on entry never matter.
-size_t prefill_scratch(const h2o_cache_desc* c, int64_t T) {
-  const size_t rows = (size_t)units_of(c) * (size_t)T;
-  return 2 * round_up(rows * sizeof(float), kWsAlign);
+// Workspace: scratch shared by prefill (column-sum partial rows and the column sums; the
+// fp32 path also keeps each row's log-sum-exp) and the split decode (per-split partials and
+// logits); its contents on entry never matter.
+int part_rows_of(const h2o_cache_desc* c, int64_t T) {
+  return c->dtype == H2O_F32 ? (int)(T > 0 ? T : 1) : h2o::kPrefillPartRows;
 }
+struct PrefillLayout {
+  size_t lse2, colpart, colsum, total;   // byte offsets of the parts, total size
+};
+PrefillLayout prefill_layout(const h2o_cache_desc* c, int64_t T) {
+  const size_t units = (size_t)units_of(c);
+  const size_t rows = round_up(units * (size_t)T * sizeof(float), kWsAlign);
+  const size_t part = round_up(
+      units * (size_t)h2o::colpart_stride(T, part_rows_of(c, T)) * sizeof(float), kWsAlign);
+  PrefillLayout l{};
+  l.lse2 = 0;
+  l.colpart = c->dtype == H2O_F32 ? rows : 0;
+  l.colsum = l.colpart + part;
+  l.total = l.colsum + rows;
+  return l;
+}
+size_t prefill_scratch(const h2o_cache_desc* c, int64_t T) { return prefill_layout(c, T).total; }
 
 size_t decode_scratch(const h2o_cache_desc* c) {
   return h2o::decode_scratch_bytes((int)elem_bytes(c->dtype), c->head_dim, slots_of(c),
@@ -144,13 +160,14 @@ h2o_status h2o_prefill(const h2o_cache_desc* c, const void* q, const void* k, co
 
   const hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
-  const size_t rows_bytes = round_up((size_t)units * T * sizeof(float), kWsAlign);
-  float* lse2 = reinterpret_cast<float*>(ws);
-  float* colsum = colsum_out ? colsum_out : reinterpret_cast<float*>(ws + rows_bytes);
+  const PrefillLayout lay = prefill_layout(c, T);
+  float* lse2 = reinterpret_cast<float*>(ws + lay.lse2);
+  float* colpart = reinterpret_cast<float*>(ws + lay.colpart);
+  float* colsum = colsum_out ? colsum_out : reinterpret_cast<float*>(ws + lay.colsum);
   const int D = c->head_dim;
   const h2o::DType dt = dtype_of(c);
 
-  h2o::PrefillParams pp{q, k, v, out, lse2, colsum, (int32_t)units, T, qk_scale(D)};
+  h2o::PrefillParams pp{q, k, v, out, lse2, colpart, (int32_t)units, T, qk_scale(D)};
   hipError_t e;
   if (dt == h2o::DType::F32) {
     if ((e = h2o::launch_prefill_attn_f32(D, pp, s))) return hip_fail(e, "prefill attention launch");
@@ -158,11 +175,9 @@ h2o_status h2o_prefill(const h2o_cache_desc* c, const void* q, const void* k, co
   } else {
     if ((e = h2o::launch_prefill_attn_mfma(dt, D, pp, s)))
       return hip_fail(e, "prefill attention launch");
-    if ((e = h2o::launch_prefill_colsum_mfma(dt, D, pp, s)))
-      return hip_fail(e, "prefill colsum launch");
   }
-  h2o::SeedParams sp{k, v, colsum, c->k_slots, c->v_slots, c->slot_pos, c->acc_score,
-                     (int32_t)units, T, c->k_heavy, c->k_local};
+  h2o::SeedParams sp{k, v, colpart, colsum, c->k_slots, c->v_slots, c->slot_pos, c->acc_score,
+                     (int32_t)units, T, part_rows_of(c, T), c->k_heavy, c->k_local};
   if ((e = h2o::launch_seed(dt, D, sp, s))) return hip_fail(e, "seed launch");
   return H2O_OK;
 }

@@ -74,6 +74,11 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int o) {
   const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, kWave);
   return ((uint64_t)hi << 32) | lo;
 }
+// DPP lane move of a float inside 16-lane rows (all lanes active).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
 // DPP lane move of a 64-bit value inside 16-lane rows (all lanes active).
 template <int CTRL>
 __device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {

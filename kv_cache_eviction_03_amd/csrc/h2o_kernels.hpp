@@ -59,13 +59,27 @@ struct DecodeParams {
   float qk_scale;       // log2(e) / sqrt(D): logits are kept in the log2 domain
 };
 
+// Column-sum partials. The prefill leaves, per unit, one partial row per block of `pb`
+// query rows: row r holds, for each key j < min(T, (r + 1) * pb), the sum of P_ij over the
+// block's rows i, and starts at pb * r * (r + 1) / 2 within the unit's stretch. The seed
+// adds the rows that cover key j in row order.
+__host__ __device__ inline int64_t colpart_row_offset(int64_t r, int pb) {
+  return (int64_t)pb * r * (r + 1) / 2;
+}
+__host__ __device__ inline int64_t colpart_stride(int64_t T, int pb) {
+  const int64_t rows = (T + pb - 1) / pb;
+  return rows > 0 ? colpart_row_offset(rows - 1, pb) + T : 0;
+}
+// Query rows per partial row of the MFMA prefill (its attention workgroup's block).
+constexpr int kPrefillPartRows = 128;
+
 struct PrefillParams {
   const void* q;        // [units][T][D]
   const void* k;
   const void* v;
   float* out;           // [units][T][D]
-  float* lse2;          // [units][T] row log-sum-exp, log2 domain (workspace)
-  float* colsum;        // [units][T]
+  float* lse2;          // [units][T] row log-sum-exp, log2 domain (fp32 path only)
+  float* colpart;       // [units][colpart_stride(T, part_rows)] column-sum partials
   int32_t units;
   int32_t T;
   float qk_scale;       // log2(e) / sqrt(D)
@@ -74,13 +88,15 @@ struct PrefillParams {
 struct SeedParams {
   const void* k;        // prompt K/V [units][T][D]
   const void* v;
-  const float* colsum;  // [units][T]
+  const float* colpart; // [units][colpart_stride(T, part_rows)]
+  float* colsum;        // [units][T]: the summed column sums are written here
   void* k_slots;
   void* v_slots;
   int32_t* slot_pos;
   float* acc;
   int32_t units;
   int32_t T;
+  int32_t part_rows;    // query rows per partial row
   int32_t k_heavy;
   int32_t k_local;
 };
@@ -116,7 +132,6 @@ hipError_t launch_decode(DType dt, int D, const DecodeParams& p, const SplitScra
                          hipStream_t s);
 // fp16 / bf16 storage: MFMA kernels.
 hipError_t launch_prefill_attn_mfma(DType dt, int D, const PrefillParams& p, hipStream_t s);
-hipError_t launch_prefill_colsum_mfma(DType dt, int D, const PrefillParams& p, hipStream_t s);
 // fp32 storage: vector-ALU kernels.
 hipError_t launch_prefill_attn_f32(int D, const PrefillParams& p, hipStream_t s);
 hipError_t launch_prefill_colsum_f32(int D, const PrefillParams& p, hipStream_t s);

@@ -3,7 +3,8 @@
 // Same two outputs as the MFMA kernels: causal attention with each row's
 // log-sum-exp (H2O blog, ttsmallhot.github.io, §2.1.1), then the softmax
 // column sums c_j = sum_{i >= j} P_ij ("H2O Heavy-Hitter Oracle 分析", §3.1)
-// re-formed from the stored log-sum-exp in a fixed order.
+// re-formed from the stored log-sum-exp in a fixed order. The column sums are
+// written as a single partial row per unit (partial-row block = T).
 //
 // Layout: 16 rows per workgroup, 16 lanes per row, each lane owning D/16
 // consecutive dims; a logit is a 16-lane butterfly sum, so both kernels form
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(kThreads) void colsum_f32_kernel(PrefillParams p) {
     const float s = dot16<D>(qv, kv) * p.qk_scale;
     if (i >= kj) cs += fast_exp2(s - lse[i]);
   }
-  if (part == 0 && kj < T_) p.colsum[(size_t)unit * T_ + kj] = cs;
+  if (part == 0 && kj < T_) p.colpart[(size_t)unit * T_ + kj] = cs;
 }
 
 }  // namespace

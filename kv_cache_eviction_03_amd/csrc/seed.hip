@@ -14,8 +14,10 @@
 // how many positions equal to v* must be kept. One ordered ballot sweep over
 // the positions then keeps every candidate above v*, the newest of those equal
 // to v*, and the recent window, writing kept positions to slots in order.
-// Column sums are staged in LDS when they fit (T + k <= 15872 words); the seeded
-// scores are then read back from LDS.
+// The column sums arrive as partial rows (one per block of part_rows query rows);
+// the kernel adds them in row order, writes the sums out, and stages them in LDS
+// when they fit (T + k <= 15872 words); the seeded scores are then read back
+// from LDS.
 //
 // reset: slot_pos = -1, acc = 0 (blog §2.3: freeing a slot only marks it).
 #include "h2o_device.hpp"
@@ -51,10 +53,49 @@ __global__ __launch_bounds__(kThreads) void seed_kernel(SeedParams p) {
   const int unit = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int T_ = p.T, k = p.k_heavy + p.k_local;
-  const float* c = p.colsum + (size_t)unit * T_;
+  float* c = p.colsum + (size_t)unit * T_;
   int* slot_of = lds_dyn;
   unsigned* bits = reinterpret_cast<unsigned*>(lds_dyn + k);
   const bool staged = stage_bits(T_, k);
+
+  // c_j = sum of the partial rows r >= j / part_rows, in row order. JB positions per thread
+  // and RR rows per batch, all loads of a batch in flight together (branch-free: loads
+  // outside the triangle read the stretch's first word and are dropped).
+  {
+    constexpr int JB = 2, RR = 8;
+    const int pb = p.part_rows, nr = (T_ + pb - 1) / pb;
+    const float* part = p.colpart + (size_t)unit * colpart_stride(T_, pb);
+    for (int j0 = 0; j0 < T_; j0 += JB * kThreads) {
+      float sum[JB];
+#pragma unroll
+      for (int a = 0; a < JB; ++a) sum[a] = 0.f;
+      for (int r0 = j0 / pb; r0 < nr; r0 += RR) {   // rows below j0 / pb cover none of them
+        float x[JB][RR];
+#pragma unroll
+        for (int a = 0; a < JB; ++a)
+#pragma unroll
+          for (int rr = 0; rr < RR; ++rr) {
+            const int j = j0 + a * kThreads + tid, r = r0 + rr;
+            const bool in = j < T_ && r < nr && j < (r + 1) * pb;   // row r covers key j
+            x[a][rr] = part[in ? colpart_row_offset(r, pb) + j : 0];
+            if (!in) x[a][rr] = 0.f;
+          }
+#pragma unroll
+        for (int a = 0; a < JB; ++a)
+#pragma unroll
+          for (int rr = 0; rr < RR; ++rr) sum[a] += x[a][rr];
+      }
+#pragma unroll
+      for (int a = 0; a < JB; ++a) {
+        const int j = j0 + a * kThreads + tid;
+        if (j < T_) {
+          c[j] = sum[a];
+          if (staged) bits[j] = __float_as_uint(sum[a]);
+        }
+      }
+    }
+  }
+  __syncthreads();                              // the sums are visible to the whole workgroup
 
   int n_keep;
   if (T_ <= k) {
@@ -62,8 +103,6 @@ __global__ __launch_bounds__(kThreads) void seed_kernel(SeedParams p) {
     for (int s = tid; s < T_; s += kThreads) slot_of[s] = s;
   } else {
     const int ncand = T_ - p.k_local;
-    if (staged)                                 // all T: the seeded scores are read back from here
-      for (int j = tid; j < T_; j += kThreads) bits[j] = __float_as_uint(c[j]);
     auto key = [&](int j) -> unsigned { return staged ? bits[j] : __float_as_uint(c[j]); };
 
     unsigned prefix = 0, mask = 0, want = (unsigned)p.k_heavy, eq_total = 0;

@@ -41,10 +41,24 @@ def test_status_strings():
     assert h2o.h2o_status_str(h2o.H2O_ERR_WORKSPACE) == "H2O_ERR_WORKSPACE"
 
 
+def round256(n):
+    return (n + 255) // 256 * 256
+
+
 def test_workspace_bytes():
     d = desc()
-    # log-sum-exp and column-sum scratch: 2 * round_up(B*H*T*4, 256)
-    assert h2o.h2o_workspace_bytes(d, 512) == 2 * ((2 * 3 * 512 * 4 + 255) // 256 * 256)
+    units, T = 2 * 3, 512
+    # fp16/bf16: partial column-sum rows of 128, 256, 384 and 512 keys (one per
+    # 128-row query block), then the column sums
+    assert h2o.h2o_workspace_bytes(d, T) == (round256(units * (128 + 256 + 384 + 512) * 4)
+                                             + round256(units * T * 4))
+    # ragged last block: 128 + 256 + 300 keys
+    assert h2o.h2o_workspace_bytes(d, 300) == (round256(units * (128 + 256 + 300) * 4)
+                                               + round256(units * 300 * 4))
+    # fp32: row log-sum-exps, one partial row of T keys, the column sums
+    assert h2o.h2o_workspace_bytes(desc(dtype=h2o.H2O_F32), T) == 3 * round256(units * T * 4)
+    sizes = [h2o.h2o_workspace_bytes(d, t) for t in range(0, 1200, 37)]
+    assert sizes == sorted(sizes)                 # a workspace for T serves every shorter prompt
     assert h2o.h2o_workspace_bytes(d, 0) == 0
     assert h2o.h2o_workspace_bytes(d, -1) == 0
     assert h2o.h2o_workspace_bytes(desc(head_dim=96), 16) == 0

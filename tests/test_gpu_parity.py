@@ -81,6 +81,21 @@ def test_small_shapes_every_unit(w):
     announce(f"[parity] {w.name}: {agg['prefill_out']:.2e} {agg['decode_out']:.2e} ties={len(agg['ties'])}")
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_prefill_early_keys_dominate(dtype):
+    # Keys 0..3 get a large component along a direction every query shares, so each row's
+    # largest logits (about 10 above the rest) sit in its first key tile, far from the
+    # diagonal: the row max found on the diagonal tile must be raised late in the row.
+    w = Workload(98, f"early-dominant-{dtype}", 1, 1, 3, 128, dtype, 300, 8, 20, 20)
+    announce(f"[parity] {w.name}: T={w.prompt}, keys 0..3 dominate every row")
+    x = gen(w)
+    x["q_prompt"][..., 0] += 3.0
+    x["k_prompt"][:, :, 0:4, 0] = 40.0
+    r = run_gpu(w, x)
+    agg = check_units(w, x, r, range(w.units_per_layer))
+    announce(f"[parity] {w.name}: prefill {agg['prefill_out']:.2e} colsum {agg['colsum_rel']:.2e}")
+
+
 def test_llama7b_layer_bf16_sampled_units():
     w = WORKLOADS[3]
     for layer in (0, 31):
