@@ -89,7 +89,7 @@ def prefill_bytes_per_unit(w) -> int:
     return 3 * T * d * s + 4 * T * d + 4 * T + 2 * k * d * s + 8 * k
 
 
-def prefill_mfma_probe(reps=3):
+def prefill_mfma_probe(reps=10, warmup=3):
     """Prefill of the OPT-30B-shaped layer (T = 2048, MFMA-bound) timed with HIP events."""
     import torch
 
@@ -101,7 +101,8 @@ def prefill_mfma_probe(reps=3):
                  max_prompt=w.prompt)
     out = torch.empty((w.batch, w.heads, w.prompt, w.head_dim), dtype=torch.float32, device="cuda:0")
     cs = torch.empty((w.batch, w.heads, w.prompt), dtype=torch.float32, device="cuda:0")
-    c.prefill(x["q_prompt"], x["k_prompt"], x["v_prompt"], out=out, colsum=cs)
+    for _ in range(warmup):                     # the shader clock ramps over the first calls
+        c.prefill(x["q_prompt"], x["k_prompt"], x["v_prompt"], out=out, colsum=cs)
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()

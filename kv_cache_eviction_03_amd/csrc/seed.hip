@@ -14,6 +14,9 @@
 // how many positions equal to v* must be kept. One ordered ballot sweep over
 // the positions then keeps every candidate above v*, the newest of those equal
 // to v*, and the recent window, writing kept positions to slots in order.
+// Copies: the recent window's K/V rows (every row when T <= k) go to slots known
+// in advance, so they are issued first and overlap the column-sum reads and the
+// selection; the heavy rows follow the selection.
 // The column sums arrive as partial rows (one per block of part_rows query rows);
 // the kernel adds them in row order, writes the sums out, and stages them in LDS
 // when they fit (T + k <= 15872 words); the seeded scores are then read back
@@ -58,6 +61,44 @@ __global__ __launch_bounds__(kThreads) void seed_kernel(SeedParams p) {
   unsigned* bits = reinterpret_cast<unsigned*>(lds_dyn + k);
   const bool staged = stage_bits(T_, k);
 
+  constexpr int CPR = D * (int)sizeof(T) / 16;   // 16-byte chunks per row
+  constexpr int VEC = 16 / (int)sizeof(T);
+  constexpr int B = 4;                           // copies in flight per thread (more measured slower)
+  const T* K = static_cast<const T*>(p.k) + (size_t)unit * T_ * D;
+  const T* V = static_cast<const T*>(p.v) + (size_t)unit * T_ * D;
+  T* ks = static_cast<T*>(p.k_slots) + (size_t)unit * k * D;
+  T* vs = static_cast<T*>(p.v_slots) + (size_t)unit * k * D;
+  // Rows whose slot is known before the selection: every row when T <= k (slot = position),
+  // else the recent window (positions T - k_local.., slots k_heavy..). Their first batch
+  // of loads is issued now and lands while the column sums are formed.
+  const int nfix = T_ <= k ? T_ : p.k_local;
+  const int fsrc = T_ <= k ? 0 : T_ - p.k_local, fdst = T_ <= k ? 0 : p.k_heavy;
+  const int ftotal = nfix * CPR;
+  uint4 kf[B], vf[B];
+  auto load_fix = [&](int base) {
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      const int idx = base + i * kThreads + tid;
+      const int r = idx < ftotal ? idx / CPR : 0, ch = idx < ftotal ? idx - r * CPR : 0;
+      const size_t src = (size_t)(fsrc + r) * D + ch * VEC;
+      kf[i] = ld16(K + src);
+      vf[i] = ld16(V + src);
+    }
+  };
+  auto store_fix = [&](int base) {
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      const int idx = base + i * kThreads + tid;
+      if (idx < ftotal) {
+        const int r = idx / CPR, ch = idx - r * CPR;
+        const size_t dst = (size_t)(fdst + r) * D + ch * VEC;
+        st16(ks + dst, kf[i]);
+        st16(vs + dst, vf[i]);
+      }
+    }
+  };
+  load_fix(0);
+
   // c_j = sum of the partial rows r >= j / part_rows, in row order. JB positions per thread
   // and RR rows per batch, all loads of a batch in flight together (branch-free: loads
   // outside the triangle read the stretch's first word and are dropped).
@@ -94,6 +135,11 @@ __global__ __launch_bounds__(kThreads) void seed_kernel(SeedParams p) {
         }
       }
     }
+  }
+  store_fix(0);
+  for (int base = B * kThreads; base < ftotal; base += B * kThreads) {
+    load_fix(base);
+    store_fix(base);
   }
   __syncthreads();                              // the sums are visible to the whole workgroup
 
@@ -214,14 +260,8 @@ __global__ __launch_bounds__(kThreads) void seed_kernel(SeedParams p) {
       acc[s] = 0.f;
     }
   }
-  constexpr int CPR = D * (int)sizeof(T) / 16;   // 16-byte chunks per row
-  constexpr int VEC = 16 / (int)sizeof(T);
-  constexpr int B = 4;                           // copies in flight per thread (more measured slower)
-  const T* K = static_cast<const T*>(p.k) + (size_t)unit * T_ * D;
-  const T* V = static_cast<const T*>(p.v) + (size_t)unit * T_ * D;
-  T* ks = static_cast<T*>(p.k_slots) + (size_t)unit * k * D;
-  T* vs = static_cast<T*>(p.v_slots) + (size_t)unit * k * D;
-  const int total = n_keep * CPR;
+  // The heavy rows (slots [0, k_heavy) when T > k), gathered by the selection.
+  const int total = (T_ > k ? p.k_heavy : 0) * CPR;
   for (int base = 0; base < total; base += B * kThreads) {
     uint4 kr[B], vr[B];
 #pragma unroll
