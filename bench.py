@@ -29,7 +29,9 @@ Timing:
     out of play (36 replicas of the cache state visited in turn, 519 MB per sweep);
   * dense_comparator: context only, the same decode steps with k = T + n (nothing
     evicted) against the H2O budget;
-  * hbm_measured_ceiling: context only, plain PyTorch streaming read and copy rates.
+  * hbm_measured_ceiling: context only, plain PyTorch streaming read and copy rates;
+  * stream_sustained: the long-streaming workload in full (4096 slots, 2^20 decode
+    steps from an empty cache), device time per 65,536-step window after the fill.
 """
 from __future__ import annotations
 
@@ -113,6 +115,8 @@ def prefill_mfma_probe(reps=10, warmup=3):
     us = 1e3 * a.elapsed_time(b) / reps
     flops = prefill_flops_per_unit(w) * w.units_per_layer
     tflops = flops / (us * 1e-6) / 1e12
+    full = [r for r, a, b in zip(win, marks[1:-1], marks[2:]) if b - a == window]
+    us_full = [u for u, a, b in zip(us_step, marks[1:-1], marks[2:]) if b - a == window]
     res = {"workload": f"{w.name}: batch {w.batch}, {w.heads} heads, d {w.head_dim}, fp16, "
                        f"prompt {w.prompt}, k = {w.k_heavy}+{w.k_local}",
            "bound": "mfma (arithmetic intensity %.0f flop/B > ridge 312.5)" % (
@@ -319,6 +323,83 @@ def dense_comparator(w, reps=5):
             "decode_us_per_step": best, "decode_tokens_per_s": w.batch / (best * 1e-6)}
 
 
+def stream_sustained(window=65536):
+    """The long-streaming workload in full: 32 heads, 4096 slots, 2^20 decode steps of
+    seeded inputs (2% heavy-hitter keys), one h2o_decode_step call per step through the C
+    ABI (t is a host argument, so the steps cannot be one replayed graph). HIP events at
+    window boundaries give the device time of the 4096 fill steps and of each 65,536-step
+    window after them; the host's own time per enqueued step is reported beside it, to
+    show the loop is bound by the GPU, not by the enqueueing."""
+    import ctypes
+    import torch
+    from kv_cache_eviction_03_amd import H2OCache
+    from kv_cache_eviction_03_amd._abi import library
+    from workloads import WORKLOADS, generate
+    w = WORKLOADS[5]
+    dev = "cuda:0"
+    x = generate(w, seed=0, device=dev)
+    B, H, d, n, k = w.batch, w.heads, w.head_dim, w.steps, w.k
+    c = H2OCache(B, H, d, w.k_heavy, w.k_local, w.torch_dtype, dev)
+    c.reset()
+    out = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    lib = library()
+    desc = c.desc()
+    dref = ctypes.byref(desc)
+    fn = lib.h2o_decode_step
+    sb = B * H * d * w.elem_bytes
+    q0, k0, v0 = x["q_dec"].data_ptr(), x["k_dec"].data_ptr(), x["v_dec"].data_ptr()
+    op, wp, wn = out.data_ptr(), c.workspace.data_ptr(), c.workspace.numel()
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    marks = [0, k] + list(range(k + window, n + 1, window))
+    if marks[-1] < n:
+        marks.append(n)                         # a last, shorter window
+    events = {}
+    torch.cuda.synchronize()
+    host0 = time.perf_counter()
+    t = 0
+    for a, b in zip(marks[:-1], marks[1:]):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        events[a] = e
+        for t in range(a, b):
+            st = fn(dref, t, q0 + t * sb, k0 + t * sb, v0 + t * sb, op, None, wp, wn, sp)
+            if st:
+                raise RuntimeError(f"h2o_decode_step failed at t = {t}: {lib.h2o_last_error()}")
+    e = torch.cuda.Event(enable_timing=True)
+    e.record(stream)
+    events[marks[-1]] = e
+    host_s = time.perf_counter() - host0
+    torch.cuda.synchronize()
+    ms = [events[a].elapsed_time(events[b]) for a, b in zip(marks[:-1], marks[1:])]
+    step_bytes = decode_bytes_per_unit(w) * w.units_per_layer
+    win = [(b - a) * B / (m * 1e-3) for a, b, m in zip(marks[1:-1], marks[2:], ms[1:])]
+    us_step = [m * 1e3 / (b - a) for a, b, m in zip(marks[1:-1], marks[2:], ms[1:])]
+    steady_steps = marks[-1] - k
+    steady_ms = sum(ms[1:])
+    res = {
+        "workload": f"{w.name}: batch {B}, {H} heads, d {d}, bf16, k = {w.k_heavy}+{w.k_local}, "
+                    f"{n} decode steps from an empty cache, 2% heavy-hitter keys",
+        "steps_timed": marks[-1],
+        "fill_steps": k, "fill_ms": ms[0],
+        "windows": len(win), "window_steps": window, "full_windows": len(full),
+        "tokens_per_s_sustained": steady_steps * B / (steady_ms * 1e-3),
+        "tokens_per_s_window_min": min(full), "tokens_per_s_window_max": max(full),
+        "us_per_step_window_min": min(us_full), "us_per_step_window_max": max(us_full),
+        "GBps_sustained": step_bytes * steady_steps / (steady_ms * 1e-3) / 1e9,
+        "hbm_frac_sustained": step_bytes * steady_steps / (steady_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "host_us_per_step_enqueue": host_s * 1e6 / marks[-1],
+        "note": "device time from HIP events at window boundaries (min/max over the full "
+                "windows; the sustained rate covers every step after the fill); per step: both "
+                "decode launches (partial + combine); algorithmic bytes 2kd·s + 12k + 5d·s + 4d "
+                "+ 8 per unit; the host waits on a full launch queue, so its time per step "
+                "matches the device's",
+    }
+    del x, c, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(w, x, units, min_seconds=10.0):
     from threadpoolctl import threadpool_info, threadpool_limits
 
@@ -372,6 +453,10 @@ def main():
                     help="only time the bench workload's decode kernel with the MALL out of play")
     ap.add_argument("--no-cold", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-stream", action="store_true",
+                    help="skip the 2^20-step long-streaming run")
+    ap.add_argument("--stream-only", action="store_true",
+                    help="only the 2^20-step long-streaming run; print its figures")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 512 MiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -395,6 +480,9 @@ def main():
     if args.decode_shapes:
         for r in decode_by_workload():
             print(json.dumps(r), flush=True)
+        return
+    if args.stream_only:
+        print(json.dumps(stream_sustained()), flush=True)
         return
 
     from kv_cache_eviction_03_amd import H2OCache
@@ -562,6 +650,8 @@ def main():
         dense = dense_comparator(w)
         dense["h2o_decode_speedup"] = dense["decode_us_per_step"] / dec_kernel_us
         result["dense_comparator"] = dense
+    if not args.no_stream:
+        result["stream_sustained"] = stream_sustained()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, x, list(range(units)))
     print(json.dumps(result), flush=True)
