@@ -115,8 +115,6 @@ def prefill_mfma_probe(reps=10, warmup=3):
     us = 1e3 * a.elapsed_time(b) / reps
     flops = prefill_flops_per_unit(w) * w.units_per_layer
     tflops = flops / (us * 1e-6) / 1e12
-    full = [r for r, a, b in zip(win, marks[1:-1], marks[2:]) if b - a == window]
-    us_full = [u for u, a, b in zip(us_step, marks[1:-1], marks[2:]) if b - a == window]
     res = {"workload": f"{w.name}: batch {w.batch}, {w.heads} heads, d {w.head_dim}, fp16, "
                        f"prompt {w.prompt}, k = {w.k_heavy}+{w.k_local}",
            "bound": "mfma (arithmetic intensity %.0f flop/B > ridge 312.5)" % (
@@ -377,6 +375,8 @@ def stream_sustained(window=65536):
     us_step = [m * 1e3 / (b - a) for a, b, m in zip(marks[1:-1], marks[2:], ms[1:])]
     steady_steps = marks[-1] - k
     steady_ms = sum(ms[1:])
+    full = [r for r, a, b in zip(win, marks[1:-1], marks[2:]) if b - a == window]
+    us_full = [u for u, a, b in zip(us_step, marks[1:-1], marks[2:]) if b - a == window]
     res = {
         "workload": f"{w.name}: batch {B}, {H} heads, d {d}, bf16, k = {w.k_heavy}+{w.k_local}, "
                     f"{n} decode steps from an empty cache, 2% heavy-hitter keys",
