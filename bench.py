@@ -30,6 +30,8 @@ Timing:
   * dense_comparator: context only, the same decode steps with k = T + n (nothing
     evicted) against the H2O budget;
   * hbm_measured_ceiling: context only, plain PyTorch streaming read and copy rates;
+  * llama_stack_decode: the LLaMA-7B-shaped model's decode step, 32 layers each with
+    its own prefilled cache (3.69 GB of slots per step, far beyond the MALL);
   * stream_sustained: the long-streaming workload in full (4096 slots, 2^20 decode
     steps from an empty cache), device time per 65,536-step window after the fill.
 """
@@ -177,6 +179,67 @@ def decode_by_workload(ids=(2, 3, 4, 5), n=32, reps=5):
                     "decode_tokens_per_s": w.batch / (best * 1e-6)})
         del x, c, out, g
         torch.cuda.empty_cache()
+    return res
+
+
+def llama_stack_decode(steps=16, reps=3):
+    """The LLaMA-7B-shaped stack in full: 32 layers (batch 64, 32 heads, d 128, bf16,
+    k = 52 + 52), each with its own cache prefilled from its own seeded 512-token prompt.
+    One decode step of the model runs the 32 layers' decode launches in turn, 3.69 GB of
+    slots per step (14x the MALL), so every launch reads its layer's slots from HBM.
+    `steps` such steps are captured as one graph; each timed replay starts from the saved
+    post-prefill state of every layer."""
+    import torch
+
+    from kv_cache_eviction_03_amd import H2OCache
+    from workloads import WORKLOADS, generate
+    dev = "cuda:0"
+    w = WORKLOADS[3].scaled(steps=steps)
+    caches, dec, snaps = [], [], []
+    for layer in range(w.layers):
+        x = generate(w, seed=0, layer=layer, device=dev)
+        c = H2OCache(w.batch, w.heads, w.head_dim, w.k_heavy, w.k_local, w.torch_dtype, dev,
+                     max_prompt=w.prompt)
+        c.reset()
+        c.prefill(x["q_prompt"], x["k_prompt"], x["v_prompt"], want_colsum=False)
+        caches.append(c)
+        dec.append((x["q_dec"], x["k_dec"], x["v_dec"]))
+        snaps.append({k: (v.clone() if torch.is_tensor(v) else v) for k, v in c.state().items()})
+        del x
+    torch.cuda.synchronize()
+    out = torch.empty((w.batch, w.heads, w.head_dim), dtype=torch.float32, device=dev)
+    side = torch.cuda.Stream(dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for i in range(steps):
+                for c, (q, k, v) in zip(caches, dec):
+                    c.decode(q[i], k[i], v[i], out=out)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        for c, st in zip(caches, snaps):
+            c.load_state(st)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        times.append(1e3 * a.elapsed_time(b) / steps)
+    us = sorted(times)[len(times) // 2]
+    byt = decode_bytes_per_unit(w) * w.units_per_layer * w.layers
+    res = {"workload": f"{w.name}: {w.layers} layers, batch {w.batch}, {w.heads} heads, "
+                       f"d {w.head_dim}, bf16, prompt {w.prompt}, k = {w.k_heavy}+{w.k_local}",
+           "us_per_model_step": us, "us_per_model_step_best": min(times),
+           "us_per_layer_launch": us / w.layers,
+           "decode_tokens_per_s": w.batch / (us * 1e-6),
+           "algorithmic_GB_per_step": byt / 1e9,
+           "GBps": byt / (us * 1e-6) / 1e9, "hbm_frac": byt / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+           "note": f"{steps} model steps (x {w.layers} layer launches) as one graph, median of "
+                   f"{reps} replays from the saved post-prefill state; HIP events"}
+    del caches, dec, snaps, out, g
+    torch.cuda.empty_cache()
     return res
 
 
@@ -455,6 +518,10 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-stream", action="store_true",
                     help="skip the 2^20-step long-streaming run")
+    ap.add_argument("--no-stack", action="store_true",
+                    help="skip the 32-layer LLaMA-7B-shaped stack decode")
+    ap.add_argument("--stack-only", action="store_true",
+                    help="only the 32-layer LLaMA-7B-shaped stack decode; print its figures")
     ap.add_argument("--stream-only", action="store_true",
                     help="only the 2^20-step long-streaming run; print its figures")
     ap.add_argument("--copy-probe", action="store_true",
@@ -483,6 +550,9 @@ def main():
         return
     if args.stream_only:
         print(json.dumps(stream_sustained()), flush=True)
+        return
+    if args.stack_only:
+        print(json.dumps(llama_stack_decode()), flush=True)
         return
 
     from kv_cache_eviction_03_amd import H2OCache
@@ -650,6 +720,8 @@ def main():
         dense = dense_comparator(w)
         dense["h2o_decode_speedup"] = dense["decode_us_per_step"] / dec_kernel_us
         result["dense_comparator"] = dense
+    if not args.no_stack:
+        result["llama_stack_decode"] = llama_stack_decode()
     if not args.no_stream:
         result["stream_sustained"] = stream_sustained()
     if not args.no_cpu_baseline:
