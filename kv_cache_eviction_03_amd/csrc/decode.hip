@@ -146,9 +146,9 @@ __device__ __forceinline__ uint64_t score_key(float a, int pos) {
 // ------------------------------------------------------------------ resident --
 
 template <typename T, int D, int THREADS>
-// Register budget: at most 128 VGPRs for the 256-thread shape, so four workgroups share a
-// CU (the bf16 build needs 131 otherwise, three per CU; measured 3.5% faster on the
-// 32-layer LLaMA-7B-shaped stack, where 2048 workgroups then run in two full rounds).
+// Register budget: at most 128 VGPRs for the 256-thread shape, so that at least four
+// workgroups share a CU (three per CU measured 3.5% slower on the 32-layer LLaMA-7B-shaped
+// stack). The kernels currently need about 92.
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS == 256 ? 4 : 1, 8)))
 void decode_resident_kernel(DecodeParams p) {
   using S = Shape<T, D, THREADS>;
