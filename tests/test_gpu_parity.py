@@ -68,6 +68,9 @@ SMALL = [
     Workload(88, "split-f32-d128", 1, 1, 2, 128, "f32", 280, 40, 150, 150),
     # bf16 d=64 with k = 1500: six 256-slot chunks; 1024-thread combine loops over slots
     Workload(89, "split-bf16-d64", 1, 1, 2, 64, "bf16", 1400, 150, 750, 750, heavy_frac=0.05),
+    # k = 8192 (the maximum), fp32 d=128: 129 split workgroups per unit (the combine's
+    # partial-out loop past its first 64 splits) and 8192 slots (its score loop past 4096)
+    Workload(86, "maxk-f32-d128", 1, 1, 1, 128, "f32", 8400, 4, 8000, 192),
     # T + k = 15900 words: the seed keeps the column sums in global memory, not LDS
     # (63 partial column-sum rows; 7700 heavy rows gathered after the selection)
     Workload(87, "unstaged-seed-f16-d64", 1, 1, 1, 64, "f16", 8000, 3, 7700, 200),
