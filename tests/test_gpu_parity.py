@@ -102,6 +102,21 @@ def test_prefill_early_keys_dominate(dtype):
     announce(f"[parity] {w.name}: prefill {agg['prefill_out']:.2e} colsum {agg['colsum_rel']:.2e}")
 
 
+BOUNDARY_T = [1, 31, 32, 33, 63, 64, 65, 127, 128, 129, 191, 255, 256, 257]
+
+
+@pytest.mark.parametrize("dtype,d", [("f16", 128), ("bf16", 64)])
+def test_prefill_tile_boundaries(dtype, d):
+    # Prompt lengths around the 32-key (pass 2) and 64-key (pass 1) tiles and the 128-row
+    # query blocks of the prefill kernel, each followed by a few decode steps.
+    for T in BOUNDARY_T:
+        w = Workload(85, f"boundary-{dtype}-d{d}-T{T}", 1, 1, 2, d, dtype, T, 3, 8, 8)
+        announce(f"[parity] {w.name}")
+        x = gen(w)
+        r = run_gpu(w, x)
+        check_units(w, x, r, range(w.units_per_layer))
+
+
 def test_llama7b_layer_bf16_sampled_units():
     w = WORKLOADS[3]
     for layer in (0, 31):
