@@ -203,15 +203,19 @@ void decode_resident_kernel(DecodeParams p) {
   // wave-uniform folds (lane r holds group r and r + 64, one exp2 per lane) into the
   // wave's own LDS copy, so no further barrier is needed.
   static_assert(ROWS <= 2 * kWave, "at most two row groups per lane");
-  const float m_a = lane < ROWS ? s_m[lane] : -INFINITY;
-  const float m_b = lane + kWave < ROWS ? s_m[lane + kWave] : -INFINITY;
+  // Every LDS read of this stretch is issued here (clamped indices), one round trip.
+  const bool in_a = lane < ROWS, in_b = lane + kWave < ROWS;
+  const float m_a0 = s_m[in_a ? lane : 0], m_b0 = s_m[in_b ? lane + kWave : 0];
+  const float l_a0 = s_l[in_a ? lane : 0], l_b0 = s_l[in_b ? lane + kWave : 0];
+  const float lg_new = s_logit[n], lg_own = s_logit[own ? jo : 0];
+  const float m_a = in_a ? m_a0 : -INFINITY;
+  const float m_b = in_b ? m_b0 : -INFINITY;
   const float M = wave_max_uniform(fmaxf(m_a, m_b));
   const float sc_a = m_a == -INFINITY ? 0.f : fast_exp2(m_a - M);
   const float sc_b = m_b == -INFINITY ? 0.f : fast_exp2(m_b - M);
-  const float l_ab = (lane < ROWS ? s_l[lane] * sc_a : 0.f) +
-                     (lane + kWave < ROWS ? s_l[lane + kWave] * sc_b : 0.f);
+  const float l_ab = (in_a ? l_a0 * sc_a : 0.f) + (in_b ? l_b0 * sc_b : 0.f);
   const float inv = __builtin_amdgcn_rcpf(wave_sum_uniform(l_ab));
-  const float p_new = fast_exp2(s_logit[n] - M) * inv;
+  const float p_new = fast_exp2(lg_new - M) * inv;
   if (lane < ROWS) s_scw[wave][lane] = sc_a;
   if (lane + kWave < ROWS) s_scw[wave][lane + kWave] = sc_b;
 
@@ -235,7 +239,7 @@ void decode_resident_kernel(DecodeParams p) {
   uint64_t key = ~0ull;
   float a = 0.f;
   if (own) {
-    a = acc_old + fast_exp2(s_logit[jo] - M) * inv;
+    a = acc_old + fast_exp2(lg_own - M) * inv;
     acc[jo] = a;
     if (full && pos_old <= limit) key = score_key(a, pos_old);
   }
