@@ -181,6 +181,41 @@ h2o_status h2o_decode_step(const h2o_cache_desc* cache, int64_t t, const void* q
                            const h2o_decode_aux* aux, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/*
+ * h2o_prefill_ragged - h2o_prefill for a batch whose sequences have their own
+ * prompt lengths (the pages' summarisation runs use prompts of varying length;
+ * H2O blog §3.2.2).
+ *   T_max       rows stored per sequence: q, k, v, out and colsum_out are laid
+ *               out as in h2o_prefill with T = T_max
+ *   lens        [batch] int32 device array, 4-byte aligned: sequence b's prompt
+ *               is its first lens[b] rows (0 <= lens[b] <= T_max; values outside
+ *               are clamped to that range on the device, never checked on the host)
+ *   workspace   at least h2o_workspace_bytes(cache, T_max) bytes
+ * Every unit of sequence b is prefilled and seeded exactly as h2o_prefill does
+ * with T = lens[b]; rows lens[b] .. T_max - 1 of out and colsum_out are not
+ * written. A sequence with lens[b] = 0 gets every slot marked free. The other
+ * arguments, errors and limits are those of h2o_prefill (with T = T_max).
+ */
+h2o_status h2o_prefill_ragged(const h2o_cache_desc* cache, const void* q, const void* k,
+                              const void* v, int32_t T_max, const int32_t* lens, float* out,
+                              float* colsum_out, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
+ * h2o_decode_step_ragged - h2o_decode_step for a batch whose sequences sit at
+ * their own positions.
+ *   t           [batch] int32 device array, 4-byte aligned: sequence b's token
+ *               goes to position t[b] (clamped to [0, H2O_MAX_POSITION - 1] on
+ *               the device); successive calls must advance every t[b] by one,
+ *               which the caller does (the library keeps no state)
+ * Every unit of sequence b takes exactly the step h2o_decode_step takes at
+ * t = t[b]. The other arguments and errors are those of h2o_decode_step.
+ */
+h2o_status h2o_decode_step_ragged(const h2o_cache_desc* cache, const int32_t* t, const void* q,
+                                  const void* k_new, const void* v_new, float* out,
+                                  const h2o_decode_aux* aux, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
 /* Static string naming a status code. */
 const char* h2o_status_str(h2o_status status);
 

@@ -18,7 +18,7 @@ H2O_F32, H2O_F16, H2O_BF16 = range(3)
 H2O_MAX_SLOTS = 8192
 
 EXPORTS = ("h2o_reset", "h2o_workspace_bytes", "h2o_prefill", "h2o_decode_step",
-           "h2o_status_str", "h2o_last_error")
+           "h2o_prefill_ragged", "h2o_decode_step_ragged", "h2o_status_str", "h2o_last_error")
 
 
 class CacheDesc(ctypes.Structure):
@@ -62,6 +62,14 @@ def library() -> ctypes.CDLL:
         lib.h2o_decode_step.argtypes = [P(CacheDesc), c_int64, c_void_p, c_void_p, c_void_p,
                                         c_void_p, P(DecodeAux), c_void_p, c_size_t, c_void_p]
         lib.h2o_decode_step.restype = c_int32
+        lib.h2o_prefill_ragged.argtypes = [P(CacheDesc), c_void_p, c_void_p, c_void_p, c_int32,
+                                           c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                           c_void_p]
+        lib.h2o_prefill_ragged.restype = c_int32
+        lib.h2o_decode_step_ragged.argtypes = [P(CacheDesc), c_void_p, c_void_p, c_void_p,
+                                               c_void_p, c_void_p, P(DecodeAux), c_void_p,
+                                               c_size_t, c_void_p]
+        lib.h2o_decode_step_ragged.restype = c_int32
         lib.h2o_status_str.argtypes = [c_int32]
         lib.h2o_status_str.restype = c_char_p
         lib.h2o_last_error.argtypes = []
@@ -90,6 +98,21 @@ def h2o_decode_step(desc: CacheDesc, t: int, q: int, k_new: int, v_new: int, out
     return library().h2o_decode_step(ctypes.byref(desc), t, q, k_new, v_new, out,
                                      ctypes.byref(aux) if aux is not None else None,
                                      workspace or None, workspace_bytes, stream)
+
+
+def h2o_prefill_ragged(desc: CacheDesc, q: int, k: int, v: int, T_max: int, lens: int, out: int,
+                       colsum_out: int, workspace: int, workspace_bytes: int, stream: int) -> int:
+    return library().h2o_prefill_ragged(ctypes.byref(desc), q, k, v, T_max, lens or None, out,
+                                        colsum_out or None, workspace or None, workspace_bytes,
+                                        stream)
+
+
+def h2o_decode_step_ragged(desc: CacheDesc, t: int, q: int, k_new: int, v_new: int, out: int,
+                           aux: DecodeAux | None, workspace: int, workspace_bytes: int,
+                           stream: int) -> int:
+    return library().h2o_decode_step_ragged(ctypes.byref(desc), t or None, q, k_new, v_new, out,
+                                            ctypes.byref(aux) if aux is not None else None,
+                                            workspace or None, workspace_bytes, stream)
 
 
 def h2o_status_str(status: int) -> str:

@@ -9,7 +9,8 @@ from __future__ import annotations
 import torch
 
 from ._abi import (H2O_BF16, H2O_F16, H2O_F32, CacheDesc, DecodeAux, check, h2o_decode_step,
-                   h2o_prefill, h2o_reset, h2o_workspace_bytes)
+                   h2o_decode_step_ragged, h2o_prefill, h2o_prefill_ragged, h2o_reset,
+                   h2o_workspace_bytes)
 
 _DTYPE_CODE = {torch.float32: H2O_F32, torch.float16: H2O_F16, torch.bfloat16: H2O_BF16}
 
@@ -102,6 +103,49 @@ class H2OCache:
                               v_new.data_ptr(), out.data_ptr(), aux, ws.data_ptr(), ws.numel(),
                               _stream(self.device)), "h2o_decode_step")
         self.t += 1
+        return out
+
+    def prefill_ragged(self, q, k, v, lens, out=None, colsum=None):
+        """q, k, v: [B, H, T_max, d]; lens: int32 [B] on the device, sequence b's prompt
+        length. Returns (out, colsum) as prefill does (rows past lens[b] are not written)
+        and sets the per-sequence positions `t_seq` to a copy of lens."""
+        T = q.shape[2]
+        shape = (self.batch, self.heads, T, self.head_dim)
+        for x, name in ((q, "q"), (k, "k"), (v, "v")):
+            self._check(x, shape, name)
+        if lens.dtype != torch.int32 or tuple(lens.shape) != (self.batch,) \
+                or not lens.is_contiguous() or lens.device != self.device:
+            raise ValueError(f"lens: expected contiguous int32 ({self.batch},) on {self.device}")
+        if out is None:
+            out = torch.empty(shape, dtype=torch.float32, device=self.device)
+        if colsum is None:
+            colsum = torch.empty(shape[:3], dtype=torch.float32, device=self.device)
+        self.reserve(T)
+        check(h2o_prefill_ragged(self.desc(), q.data_ptr(), k.data_ptr(), v.data_ptr(), T,
+                                 lens.data_ptr(), out.data_ptr(), _ptr(colsum),
+                                 self.workspace.data_ptr(), self.workspace.numel(),
+                                 _stream(self.device)), "h2o_prefill_ragged")
+        self.t_seq = lens.clone()
+        return out, colsum
+
+    def decode_ragged(self, q, k_new, v_new, out=None, victim_slot=None, evicted_pos=None,
+                      evicted_acc=None):
+        """One token per sequence at its own position t_seq[b] (device int32 [B]); advances
+        every t_seq[b] by one. Returns out [B, H, d] fp32."""
+        shape = (self.batch, self.heads, self.head_dim)
+        for x, name in ((q, "q"), (k_new, "k_new"), (v_new, "v_new")):
+            self._check(x, shape, name)
+        if out is None:
+            out = torch.empty(shape, dtype=torch.float32, device=self.device)
+        aux = None
+        if victim_slot is not None or evicted_pos is not None or evicted_acc is not None:
+            aux = DecodeAux(_ptr(victim_slot), _ptr(evicted_pos), _ptr(evicted_acc))
+        ws = self.workspace
+        check(h2o_decode_step_ragged(self.desc(), self.t_seq.data_ptr(), q.data_ptr(),
+                                     k_new.data_ptr(), v_new.data_ptr(), out.data_ptr(), aux,
+                                     ws.data_ptr(), ws.numel(), _stream(self.device)),
+              "h2o_decode_step_ragged")
+        self.t_seq += 1
         return out
 
     def state(self) -> dict:

@@ -163,7 +163,7 @@ void decode_resident_kernel(DecodeParams p) {
   const int unit = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rl = tid % LANES, g = tid / LANES;
-  const int k = p.k, t = p.t;
+  const int k = p.k, t = unit_bound(p.tpos, unit, p.heads, p.t, 0x7ffffffe);
   const int n = min(k, t);
   const bool full = n == k;
   const int limit = t - p.k_local;
@@ -292,7 +292,7 @@ __global__ __launch_bounds__(kPartThreads) void decode_split_partial_kernel(Deco
   const int unit = blockIdx.x / nsplit, sp = blockIdx.x - unit * nsplit;
   const int tid = threadIdx.x;
   const int rl = tid % LANES, g = tid / LANES;
-  const int k = p.k, n = min(k, p.t);
+  const int k = p.k, n = min(k, unit_bound(p.tpos, unit, p.heads, p.t, 0x7ffffffe));
   const T* ks = static_cast<const T*>(p.k_slots) + (size_t)unit * k * D;
   const T* vs = static_cast<const T*>(p.v_slots) + (size_t)unit * k * D;
   const T* kn = static_cast<const T*>(p.k_new) + (size_t)unit * D;
@@ -368,7 +368,7 @@ __global__ __launch_bounds__(kCombThreads) void decode_split_combine_kernel(Deco
 
   const int unit = blockIdx.x, nsplit = w.splits;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int k = p.k, t = p.t;
+  const int k = p.k, t = unit_bound(p.tpos, unit, p.heads, p.t, 0x7ffffffe);
   const int n = min(k, t);
   const bool full = n == k;
   const int limit = t - p.k_local;

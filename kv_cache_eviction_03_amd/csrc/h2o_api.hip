@@ -132,9 +132,14 @@ h2o_status h2o_reset(const h2o_cache_desc* c, void* stream) {
   return H2O_OK;
 }
 
-h2o_status h2o_prefill(const h2o_cache_desc* c, const void* q, const void* k, const void* v,
-                       int32_t T, float* out, float* colsum_out, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The prefill behind both entry points; lens = NULL means every sequence has length T.
+h2o_status prefill_impl(const h2o_cache_desc* c, const void* q, const void* k, const void* v,
+                        int32_t T, const int32_t* lens, float* out, float* colsum_out,
+                        void* workspace, size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
   if (h2o_status st = check_desc(c)) return st;
   if (T < 0) return fail(H2O_ERR_INVALID, "prompt length T = %d < 0", T);
@@ -167,7 +172,8 @@ h2o_status h2o_prefill(const h2o_cache_desc* c, const void* q, const void* k, co
   const int D = c->head_dim;
   const h2o::DType dt = dtype_of(c);
 
-  h2o::PrefillParams pp{q, k, v, out, lse2, colpart, (int32_t)units, T, qk_scale(D)};
+  h2o::PrefillParams pp{q, k, v, out, lse2, colpart, lens, (int32_t)units, c->heads, T,
+                        qk_scale(D)};
   hipError_t e;
   if (dt == h2o::DType::F32) {
     if ((e = h2o::launch_prefill_attn_f32(D, pp, s))) return hip_fail(e, "prefill attention launch");
@@ -176,15 +182,18 @@ h2o_status h2o_prefill(const h2o_cache_desc* c, const void* q, const void* k, co
     if ((e = h2o::launch_prefill_attn_mfma(dt, D, pp, s)))
       return hip_fail(e, "prefill attention launch");
   }
-  h2o::SeedParams sp{k, v, colpart, colsum, c->k_slots, c->v_slots, c->slot_pos, c->acc_score,
-                     (int32_t)units, T, part_rows_of(c, T), c->k_heavy, c->k_local};
+  h2o::SeedParams sp{k, v, colpart, colsum, lens, c->k_slots, c->v_slots, c->slot_pos,
+                     c->acc_score, (int32_t)units, c->heads, T, part_rows_of(c, T), c->k_heavy,
+                     c->k_local};
   if ((e = h2o::launch_seed(dt, D, sp, s))) return hip_fail(e, "seed launch");
   return H2O_OK;
 }
 
-h2o_status h2o_decode_step(const h2o_cache_desc* c, int64_t t, const void* q, const void* k_new,
-                           const void* v_new, float* out, const h2o_decode_aux* aux,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+// The decode step behind both entry points; tpos = NULL means every sequence is at t.
+h2o_status decode_impl(const h2o_cache_desc* c, int64_t t, const int32_t* tpos, const void* q,
+                       const void* k_new, const void* v_new, float* out,
+                       const h2o_decode_aux* aux, void* workspace, size_t workspace_bytes,
+                       void* stream) {
   g_err[0] = 0;
   if (h2o_status st = check_desc(c)) return st;
   if (t < 0 || t >= (int64_t)H2O_MAX_POSITION)
@@ -217,11 +226,50 @@ h2o_status h2o_decode_step(const h2o_cache_desc* c, int64_t t, const void* q, co
               : h2o::SplitScratch{};
   h2o::DecodeParams p{q, k_new, v_new, c->k_slots, c->v_slots, c->slot_pos, c->acc_score, out,
                       aux ? aux->victim_slot : nullptr, aux ? aux->evicted_pos : nullptr,
-                      aux ? aux->evicted_acc : nullptr, (int32_t)(c->batch * c->heads), kk,
-                      c->k_local, (int32_t)t, qk_scale(D)};
+                      aux ? aux->evicted_acc : nullptr, tpos, (int32_t)(c->batch * c->heads),
+                      c->heads, kk, c->k_local, (int32_t)t, qk_scale(D)};
   if (hipError_t e = h2o::launch_decode(dtype_of(c), D, p, w, static_cast<hipStream_t>(stream)))
     return hip_fail(e, "decode launch");
   return H2O_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+h2o_status h2o_prefill(const h2o_cache_desc* c, const void* q, const void* k, const void* v,
+                       int32_t T, float* out, float* colsum_out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  return prefill_impl(c, q, k, v, T, nullptr, out, colsum_out, workspace, workspace_bytes,
+                      stream);
+}
+
+h2o_status h2o_prefill_ragged(const h2o_cache_desc* c, const void* q, const void* k,
+                              const void* v, int32_t T_max, const int32_t* lens, float* out,
+                              float* colsum_out, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  g_err[0] = 0;
+  if (!lens || !aligned(lens, 4))
+    return fail(H2O_ERR_INVALID, "lens must be a non-NULL, 4-byte aligned device array");
+  return prefill_impl(c, q, k, v, T_max, lens, out, colsum_out, workspace, workspace_bytes,
+                      stream);
+}
+
+h2o_status h2o_decode_step(const h2o_cache_desc* c, int64_t t, const void* q, const void* k_new,
+                           const void* v_new, float* out, const h2o_decode_aux* aux,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(c, t, nullptr, q, k_new, v_new, out, aux, workspace, workspace_bytes,
+                     stream);
+}
+
+h2o_status h2o_decode_step_ragged(const h2o_cache_desc* c, const int32_t* t, const void* q,
+                                  const void* k_new, const void* v_new, float* out,
+                                  const h2o_decode_aux* aux, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  if (!t || !aligned(t, 4))
+    return fail(H2O_ERR_INVALID, "t must be a non-NULL, 4-byte aligned device array");
+  return decode_impl(c, 0, t, q, k_new, v_new, out, aux, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

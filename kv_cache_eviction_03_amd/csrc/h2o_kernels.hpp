@@ -52,12 +52,23 @@ struct DecodeParams {
   int32_t* victim_slot; // [units] or null
   int32_t* evicted_pos; // [units] or null
   float* evicted_acc;   // [units] or null
+  const int32_t* tpos;  // [batch] per-sequence positions (device), or null: t for all
   int32_t units;
+  int32_t heads;        // units of one sequence
   int32_t k;
   int32_t k_local;
   int32_t t;
   float qk_scale;       // log2(e) / sqrt(D): logits are kept in the log2 domain
 };
+
+// A unit's own bound from a per-sequence device array (clamped to [0, hi], so a bad entry
+// cannot address outside the buffers), or the shared value when there is no array.
+__device__ __forceinline__ int unit_bound(const int32_t* per_seq, int unit, int heads, int shared,
+                                          int hi) {
+  if (!per_seq) return shared;
+  const int v = per_seq[unit / heads];
+  return v < 0 ? 0 : (v > hi ? hi : v);
+}
 
 // Column-sum partials. The prefill leaves, per unit, one partial row per block of `pb`
 // query rows: row r holds, for each key j < min(T, (r + 1) * pb), the sum of P_ij over the
@@ -80,8 +91,10 @@ struct PrefillParams {
   float* out;           // [units][T][D]
   float* lse2;          // [units][T] row log-sum-exp, log2 domain (fp32 path only)
   float* colpart;       // [units][colpart_stride(T, part_rows)] column-sum partials
+  const int32_t* lens;  // [batch] per-sequence prompt lengths <= T (device), or null: T
   int32_t units;
-  int32_t T;
+  int32_t heads;        // units of one sequence
+  int32_t T;            // rows stored per unit (the stride of q, k, v, out)
   float qk_scale;       // log2(e) / sqrt(D)
 };
 
@@ -90,12 +103,14 @@ struct SeedParams {
   const void* v;
   const float* colpart; // [units][colpart_stride(T, part_rows)]
   float* colsum;        // [units][T]: the summed column sums are written here
+  const int32_t* lens;  // [batch] per-sequence prompt lengths <= T (device), or null: T
   void* k_slots;
   void* v_slots;
   int32_t* slot_pos;
   float* acc;
   int32_t units;
-  int32_t T;
+  int32_t heads;        // units of one sequence
+  int32_t T;            // rows stored per unit
   int32_t part_rows;    // query rows per partial row
   int32_t k_heavy;
   int32_t k_local;

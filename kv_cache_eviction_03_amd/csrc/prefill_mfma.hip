@@ -153,11 +153,12 @@ __device__ __forceinline__ void attn_block(const PrefillParams& p, int unit, int
   typedef f32x4 STile[RB][BNA / 16];
   typedef V8 KOps[D / 32][BNA / 16];
   typedef V8 VOps[BNA / 32][D / 16];
-  const int T_ = p.T;
+  const int Ts = p.T;                           // rows stored per unit
+  const int T_ = unit_bound(p.lens, unit, p.heads, Ts, Ts);   // this unit's prompt length
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
-  const size_t base = (size_t)unit * T_ * D;
+  const size_t base = (size_t)unit * Ts * D;
   const T* Q = static_cast<const T*>(p.q) + base;
   const T* K = static_cast<const T*>(p.k) + base;
   const T* V = static_cast<const T*>(p.v) + base;
@@ -432,7 +433,7 @@ __device__ __forceinline__ void attn_block(const PrefillParams& p, int unit, int
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float* cpart = p.colpart + (size_t)unit * colpart_stride(T_, BM) + colpart_row_offset(qb, BM);
+  float* cpart = p.colpart + (size_t)unit * colpart_stride(Ts, BM) + colpart_row_offset(qb, BM);
   // Wave 0 adds the four waves' column partials of tile kt (in wave order, skipping waves
   // that did not compute it) and stores them.
   auto flush = [&](int kt) {
@@ -558,7 +559,7 @@ __device__ __forceinline__ void attn_block(const PrefillParams& p, int unit, int
   for (int rb = 0; rb < RB; ++rb) {
     const int qrow = row0 + rb * 16 + l16;
     if (qrow < T_) {
-      float* orow = p.out + ((size_t)unit * T_ + qrow) * D;
+      float* orow = p.out + ((size_t)unit * Ts + qrow) * D;
 #pragma unroll
       for (int db = 0; db < D / 16; ++db)
         *reinterpret_cast<f32x4*>(orow + db * 16 + 4 * g) = o[rb][db];
@@ -578,7 +579,9 @@ void prefill_attn_kernel(PrefillParams p) {
   const int nqb = (p.T + BM - 1) / BM;
   const UnitBlock ub = xcd_unit_block(blockIdx.x, p.units, nqb);
   if (ub.unit >= p.units) return;
-  attn_block<T, D, RB>(p, ub.unit, nqb - 1 - ub.r, lds, cbuf);  // longest first
+  const int qb = nqb - 1 - ub.r;                // longest first
+  if (qb * BM >= unit_bound(p.lens, ub.unit, p.heads, p.T, p.T)) return;   // past this prompt
+  attn_block<T, D, RB>(p, ub.unit, qb, lds, cbuf);
 }
 
 // 16-row blocks per wave: BM = 4 waves x 16 x RB query rows per workgroup.

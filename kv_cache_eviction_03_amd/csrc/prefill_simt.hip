@@ -40,16 +40,18 @@ __device__ __forceinline__ float dot16(const float (&a)[D / 16], const float (&b
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_f32_kernel(PrefillParams p) {
   constexpr int DP = D / 16;
-  const int T_ = p.T;
-  const int nqb = (T_ + RB - 1) / RB;
+  const int Ts = p.T;
+  const int nqb = (Ts + RB - 1) / RB;
   const UnitBlock ub = xcd_unit_block(blockIdx.x, p.units, nqb);
   if (ub.unit >= p.units) return;
   const int unit = ub.unit;
+  const int T_ = unit_bound(p.lens, unit, p.heads, Ts, Ts);   // this unit's prompt length
   const int qb = nqb - 1 - ub.r;
+  if (qb * RB >= T_) return;                   // past this prompt
   const int qi = threadIdx.x / 16, part = threadIdx.x % 16;
   const int q = qb * RB + qi;
   const int qc = q < T_ ? q : T_ - 1;   // rows past T compute a copy, never stored
-  const size_t base = (size_t)unit * T_ * D;
+  const size_t base = (size_t)unit * Ts * D;
   const float* Q = static_cast<const float*>(p.q) + base;
   const float* K = static_cast<const float*>(p.k) + base;
   const float* V = static_cast<const float*>(p.v) + base;
@@ -77,27 +79,29 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(PrefillParams p) {
   }
   if (q < T_) {
     const float inv = 1.0f / l;
-    float* orow = p.out + ((size_t)unit * T_ + q) * D + part * DP;
+    float* orow = p.out + ((size_t)unit * Ts + q) * D + part * DP;
 #pragma unroll
     for (int i = 0; i < DP; ++i) orow[i] = o[i] * inv;
-    if (part == 0) p.lse2[(size_t)unit * T_ + q] = m + log2f(l);
+    if (part == 0) p.lse2[(size_t)unit * Ts + q] = m + log2f(l);
   }
 }
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void colsum_f32_kernel(PrefillParams p) {
   constexpr int DP = D / 16;
-  const int T_ = p.T;
-  const UnitBlock ub = xcd_unit_block(blockIdx.x, p.units, (T_ + RB - 1) / RB);
+  const int Ts = p.T;
+  const UnitBlock ub = xcd_unit_block(blockIdx.x, p.units, (Ts + RB - 1) / RB);
   if (ub.unit >= p.units) return;
   const int unit = ub.unit;
+  const int T_ = unit_bound(p.lens, unit, p.heads, Ts, Ts);   // this unit's prompt length
   const int kb = ub.r;
+  if (kb * RB >= T_) return;                   // past this prompt
   const int kj = kb * RB + threadIdx.x / 16, part = threadIdx.x % 16;
   const int kc = kj < T_ ? kj : T_ - 1;
-  const size_t base = (size_t)unit * T_ * D;
+  const size_t base = (size_t)unit * Ts * D;
   const float* Q = static_cast<const float*>(p.q) + base;
   const float* K = static_cast<const float*>(p.k) + base;
-  const float* lse = p.lse2 + (size_t)unit * T_;
+  const float* lse = p.lse2 + (size_t)unit * Ts;
 
   float kv[DP];
   load_part<D>(K + (size_t)kc * D, part, kv);
@@ -108,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void colsum_f32_kernel(PrefillParams p) {
     const float s = dot16<D>(qv, kv) * p.qk_scale;
     if (i >= kj) cs += fast_exp2(s - lse[i]);
   }
-  if (part == 0 && kj < T_) p.colpart[(size_t)unit * T_ + kj] = cs;
+  if (part == 0 && kj < T_) p.colpart[(size_t)unit * Ts + kj] = cs;
 }
 
 }  // namespace

@@ -33,7 +33,9 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 // Column sums are staged in LDS when slot table + sums fit in 62 KB of dynamic LDS.
 constexpr int kStageWords = 62 * 1024 / 4;
-__host__ __device__ inline bool stage_bits(int T, int k) { return T > k && T + k <= kStageWords; }
+// Ts = rows stored per unit (sizes the LDS), Tb = this unit's prompt length.
+__host__ __device__ inline bool stage_alloc(int Ts, int k) { return Ts + k <= kStageWords; }
+__host__ __device__ inline bool stage_bits(int Ts, int Tb, int k) { return Tb > k && stage_alloc(Ts, k); }
 
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ unsigned wave_prefix(unsigned v, int lane) {
@@ -55,17 +57,18 @@ __global__ __launch_bounds__(kThreads) void seed_kernel(SeedParams p) {
 
   const int unit = blockIdx.x, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int T_ = p.T, k = p.k_heavy + p.k_local;
-  float* c = p.colsum + (size_t)unit * T_;
+  const int Ts = p.T, k = p.k_heavy + p.k_local;
+  const int T_ = unit_bound(p.lens, unit, p.heads, Ts, Ts);   // this unit's prompt length
+  float* c = p.colsum + (size_t)unit * Ts;
   int* slot_of = lds_dyn;
   unsigned* bits = reinterpret_cast<unsigned*>(lds_dyn + k);
-  const bool staged = stage_bits(T_, k);
+  const bool staged = stage_bits(Ts, T_, k);
 
   constexpr int CPR = D * (int)sizeof(T) / 16;   // 16-byte chunks per row
   constexpr int VEC = 16 / (int)sizeof(T);
   constexpr int B = 4;                           // copies in flight per thread (more measured slower)
-  const T* K = static_cast<const T*>(p.k) + (size_t)unit * T_ * D;
-  const T* V = static_cast<const T*>(p.v) + (size_t)unit * T_ * D;
+  const T* K = static_cast<const T*>(p.k) + (size_t)unit * Ts * D;
+  const T* V = static_cast<const T*>(p.v) + (size_t)unit * Ts * D;
   T* ks = static_cast<T*>(p.k_slots) + (size_t)unit * k * D;
   T* vs = static_cast<T*>(p.v_slots) + (size_t)unit * k * D;
   // Rows whose slot is known before the selection: every row when T <= k (slot = position),
@@ -105,7 +108,7 @@ __global__ __launch_bounds__(kThreads) void seed_kernel(SeedParams p) {
   {
     constexpr int JB = 2, RR = 8;
     const int pb = p.part_rows, nr = (T_ + pb - 1) / pb;
-    const float* part = p.colpart + (size_t)unit * colpart_stride(T_, pb);
+    const float* part = p.colpart + (size_t)unit * colpart_stride(Ts, pb);
     for (int j0 = 0; j0 < T_; j0 += JB * kThreads) {
       float sum[JB];
 #pragma unroll
@@ -296,7 +299,7 @@ __global__ void reset_kernel(ResetParams p) {
 template <typename T, int D>
 hipError_t seed(const SeedParams& p, hipStream_t s) {
   const int k = p.k_heavy + p.k_local;
-  const size_t lds = (size_t)k * sizeof(int) + (stage_bits(p.T, k) ? (size_t)p.T * 4 : 0);
+  const size_t lds = (size_t)k * sizeof(int) + (stage_alloc(p.T, k) ? (size_t)p.T * 4 : 0);
   seed_kernel<T, D><<<dim3((unsigned)p.units), dim3(kThreads), lds, s>>>(p);
   return hipGetLastError();
 }

@@ -54,6 +54,35 @@ def run_gpu(w, x, record_steps=True):
     return r
 
 
+def run_gpu_ragged(w, x, lens):
+    """run_gpu for a ragged batch: sequence b's prompt is its first lens[b] stored rows, and
+    its decode token i sits at position lens[b] + i (h2o_prefill_ragged, then
+    h2o_decode_step_ragged)."""
+    from kv_cache_eviction_03_amd import H2OCache
+
+    B, H, d, T, n = w.batch, w.heads, w.head_dim, w.prompt, w.steps
+    dev = x["q_prompt"].device
+    cache = H2OCache(B, H, d, w.k_heavy, w.k_local, w.torch_dtype, dev, max_prompt=T)
+    cache.reset()
+    lens_d = torch.tensor(lens, dtype=torch.int32, device=dev)
+    r = {}
+    r["prefill_out"], r["colsum"] = cache.prefill_ragged(x["q_prompt"], x["k_prompt"],
+                                                         x["v_prompt"], lens_d)
+    r["pos0"] = cache.slot_pos.clone()
+    r["acc0"] = cache.acc_score.clone()
+    r["outs"] = torch.empty((n, B, H, d), dtype=torch.float32, device=dev)
+    r["victims"] = torch.empty((n, B, H), dtype=torch.int32, device=dev)
+    r["ev_pos"] = torch.empty((n, B, H), dtype=torch.int32, device=dev)
+    r["ev_acc"] = torch.empty((n, B, H), dtype=torch.float32, device=dev)
+    for i in range(n):
+        cache.decode_ragged(x["q_dec"][i], x["k_dec"][i], x["v_dec"][i], out=r["outs"][i],
+                            victim_slot=r["victims"][i], evicted_pos=r["ev_pos"][i],
+                            evicted_acc=r["ev_acc"][i])
+    torch.cuda.synchronize(dev)
+    r["cache"] = cache
+    return r
+
+
 def advance_gpu(cache, x, t1):
     """Decode steps cache.t .. t1 - 1 of x with no record kept, one direct C-ABI call per
     step (the binding's per-call checks left out, for long streams)."""
@@ -92,15 +121,18 @@ def _rel_ok(a, b, rtol):
     return np.abs(a - b) <= rtol * np.maximum(np.abs(a), np.abs(b)) + 1e-30
 
 
-def check_unit(w, x, r, b, h, steps=None):
+def check_unit(w, x, r, b, h, steps=None, prompt_len=None):
     """Replay unit (b, h) through the oracle; raise AssertionError on a mismatch.
 
+    prompt_len: the unit's own prompt length when the batch is ragged (its first
+    prompt_len stored rows; decode token i then sits at position prompt_len + i).
     Returns a dict of per-unit error figures and the tie log.
     """
     atol = OUT_ATOL[w.dtype]
-    T = w.prompt
+    T = w.prompt if prompt_len is None else int(prompt_len)
     n = w.steps if steps is None else steps
     u = unit_inputs(x, b, h)
+    u["Qp"], u["Kp"], u["Vp"] = u["Qp"][:T], u["Kp"][:T], u["Vp"][:T]
     pos0 = r["pos0"][b, h].cpu().numpy()
     acc0 = r["acc0"][b, h].cpu().numpy()
     cache = UnitCache(w.k_heavy, w.k_local, w.head_dim)
@@ -108,10 +140,10 @@ def check_unit(w, x, r, b, h, steps=None):
     if T > 0:
         kept_gpu = sorted(int(p) for p in pos0 if p >= 0)
         O, c64 = prefill(cache, u["Qp"], u["Kp"], u["Vp"], adopt_kept=kept_gpu, rel_tol=TIE_RTOL)
-        go = r["prefill_out"][b, h].double().cpu().numpy()
+        go = r["prefill_out"][b, h, :T].double().cpu().numpy()
         err["prefill_out"] = float(np.abs(go - O).max())
         assert err["prefill_out"] <= atol, f"unit ({b},{h}) prefill out err {err['prefill_out']}"
-        gc = r["colsum"][b, h].double().cpu().numpy()
+        gc = r["colsum"][b, h, :T].double().cpu().numpy()
         ok = _rel_ok(gc, c64, SCORE_RTOL)
         err["colsum_rel"] = float((np.abs(gc - c64) / np.maximum(np.abs(c64), 1e-30)).max())
         assert ok.all(), f"unit ({b},{h}) colsum mismatch at {np.nonzero(~ok)[0][:5]}"
@@ -153,12 +185,13 @@ def check_unit(w, x, r, b, h, steps=None):
     return err
 
 
-def check_units(w, x, r, units):
-    """Check a list of flat unit indices (b * H + h). Returns aggregated errors."""
+def check_units(w, x, r, units, lens=None):
+    """Check a list of flat unit indices (b * H + h); lens: per-sequence prompt lengths of
+    a ragged batch. Returns aggregated errors."""
     agg = {"prefill_out": 0.0, "decode_out": 0.0, "colsum_rel": 0.0, "acc_rel": 0.0, "ties": []}
     for uidx in units:
         b, h = divmod(int(uidx), w.heads)
-        e = check_unit(w, x, r, b, h)
+        e = check_unit(w, x, r, b, h, prompt_len=None if lens is None else lens[b])
         for k in ("prefill_out", "decode_out", "colsum_rel", "acc_rel"):
             agg[k] = max(agg[k], e[k])
         agg["ties"] += [(b, h, *t) for t in e["ties"]]

@@ -126,6 +126,37 @@ def test_decode_checks(args, status):
     assert st == status, h2o.h2o_last_error()
 
 
+@pytest.mark.parametrize("args,status", [
+    (dict(lens=0), h2o.H2O_ERR_INVALID),
+    (dict(lens=A + 2), h2o.H2O_ERR_INVALID),
+    (dict(T=-1), h2o.H2O_ERR_INVALID),
+    (dict(q=0), h2o.H2O_ERR_INVALID),
+    (dict(ws=0), h2o.H2O_ERR_WORKSPACE),
+    (dict(desc=dict(heads=0)), h2o.H2O_ERR_INVALID),
+])
+def test_prefill_ragged_checks(args, status):
+    a = dict(q=A, k=A, v=A, T=64, lens=A, out=A, colsum=0, ws=A, ws_bytes=1 << 20, desc={})
+    a.update(args)
+    st = h2o.h2o_prefill_ragged(desc(**a["desc"]), a["q"], a["k"], a["v"], a["T"], a["lens"],
+                                a["out"], a["colsum"], a["ws"], a["ws_bytes"], 0)
+    assert st == status, h2o.h2o_last_error()
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(t=0), h2o.H2O_ERR_INVALID),
+    (dict(t=A + 1), h2o.H2O_ERR_INVALID),
+    (dict(q=0), h2o.H2O_ERR_INVALID),
+    (dict(aux=DecodeAux(0, A + 2, 0)), h2o.H2O_ERR_INVALID),
+    (dict(desc=dict(k_local=0)), h2o.H2O_ERR_INVALID),
+])
+def test_decode_ragged_checks(args, status):
+    a = dict(t=A, q=A, k_new=A, v_new=A, out=A, aux=None, desc={})
+    a.update(args)
+    st = h2o.h2o_decode_step_ragged(desc(**a["desc"]), a["t"], a["q"], a["k_new"], a["v_new"],
+                                    a["out"], a["aux"], 0, 0, 0)
+    assert st == status, h2o.h2o_last_error()
+
+
 def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     import kv_cache_eviction_03_amd._abi as abi
     monkeypatch.setattr(abi, "_lib", None)

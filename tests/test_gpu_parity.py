@@ -117,6 +117,24 @@ def test_prefill_tile_boundaries(dtype, d):
         check_units(w, x, r, range(w.units_per_layer))
 
 
+@pytest.mark.parametrize("dtype,d", [("f16", 128), ("bf16", 64), ("f32", 128)])
+def test_ragged_batch(dtype, d):
+    # Sequences with their own prompt lengths (an empty prompt, one at k, one below it and
+    # two longer ones, the longest filling the stored rows), then 24 decode steps, each
+    # sequence at its own position.
+    from tests.parity import run_gpu_ragged
+    lens = [300, 0, 64, 37, 157]
+    w = Workload(84, f"ragged-batch-{dtype}-d{d}", len(lens), 1, 3, d, dtype, max(lens), 24,
+                 40, 24, heavy_frac=0.05)
+    announce(f"[parity] {w.name}: prompt lengths {lens}, k = {w.k}")
+    x = gen(w)
+    r = run_gpu_ragged(w, x, lens)
+    agg = check_units(w, x, r, range(w.units_per_layer), lens=lens)
+    assert r["cache"].t_seq.cpu().tolist() == [L + w.steps for L in lens]
+    announce(f"[parity] {w.name}: prefill {agg['prefill_out']:.2e} decode {agg['decode_out']:.2e} "
+             f"ties={len(agg['ties'])}")
+
+
 def test_llama7b_layer_bf16_sampled_units():
     w = WORKLOADS[3]
     for layer in (0, 31):
