@@ -30,6 +30,8 @@ Timing:
   * dense_comparator: context only, the same decode steps with k = T + n (nothing
     evicted) against the H2O budget;
   * hbm_measured_ceiling: context only, plain PyTorch streaming read and copy rates;
+  * ragged_step: the bench layer with seeded prompt lengths in [256, 512] through the
+    ragged entry points, against the same batch padded to 512;
   * llama_stack_decode: the LLaMA-7B-shaped model's decode step, 32 layers each with
     its own prefilled cache (3.69 GB of slots per step, far beyond the MALL);
   * stream_sustained: the long-streaming workload in full (4096 slots, 2^20 decode
@@ -239,6 +241,72 @@ def llama_stack_decode(steps=16, reps=3):
            "note": f"{steps} model steps (x {w.layers} layer launches) as one graph, median of "
                    f"{reps} replays from the saved post-prefill state; HIP events"}
     del caches, dec, snaps, out, g
+    torch.cuda.empty_cache()
+    return res
+
+
+def ragged_step(reps=20, seed=7):
+    """The bench layer shape with a ragged batch: the 8 sequences' prompt lengths are seeded
+    uniform draws in [256, 512] (stored padded to 512 rows, as a summarisation batch would
+    be), then 32 generated tokens per sequence, each at its own position. One step = reset +
+    h2o_prefill_ragged + 32 h2o_decode_step_ragged (each step's position array precomputed
+    on the device), replayed as one HIP graph; compared with the same step padded to 512
+    for every sequence (h2o_prefill + h2o_decode_step)."""
+    import numpy as np
+    import torch
+
+    from kv_cache_eviction_03_amd import H2OCache
+    from workloads import WORKLOADS, generate
+    dev = "cuda:0"
+    w = WORKLOADS[2]
+    B, H, d, T, n = w.batch, w.heads, w.head_dim, w.prompt, w.steps
+    lens = np.random.default_rng(seed).integers(256, T + 1, size=B).astype(np.int32)
+    x = generate(w, seed=0, device=dev)
+    lens_d = torch.from_numpy(lens).to(dev)
+    t_all = torch.stack([lens_d + i for i in range(n)]).contiguous()   # [n][B]
+    out_p = torch.empty((B, H, T, d), dtype=torch.float32, device=dev)
+    cs = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    outs = torch.empty((n, B, H, d), dtype=torch.float32, device=dev)
+    res = {}
+    for mode in ("ragged", "padded"):
+        c = H2OCache(B, H, d, w.k_heavy, w.k_local, w.torch_dtype, dev, max_prompt=T)
+
+        def step():
+            c.reset()
+            if mode == "ragged":
+                c.prefill_ragged(x["q_prompt"], x["k_prompt"], x["v_prompt"], lens_d,
+                                 out=out_p, colsum=cs)
+                for i in range(n):
+                    c.decode_ragged(x["q_dec"][i], x["k_dec"][i], x["v_dec"][i], out=outs[i],
+                                    t=t_all[i])
+            else:
+                c.prefill(x["q_prompt"], x["k_prompt"], x["v_prompt"], out=out_p, colsum=cs)
+                for i in range(n):
+                    c.decode(x["q_dec"][i], x["k_dec"][i], x["v_dec"][i], out=outs[i])
+        step()
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream(dev)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                step()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        us = 1e3 * a.elapsed_time(b) / reps
+        res[mode] = {"us_per_step": us, "generated_tokens_per_s": B * n / (us * 1e-6)}
+        del c, g
+    res["workload"] = (f"{w.name} shape with prompt lengths {lens.tolist()} (seeded uniform in "
+                       f"[256, {T}], stored padded to {T}), {n} generated tokens each")
+    res["prompt_tokens"] = int(lens.sum())
+    res["ragged_speedup"] = res["padded"]["us_per_step"] / res["ragged"]["us_per_step"]
+    del x, out_p, cs, outs
     torch.cuda.empty_cache()
     return res
 
@@ -518,6 +586,10 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-stream", action="store_true",
                     help="skip the 2^20-step long-streaming run")
+    ap.add_argument("--no-ragged", action="store_true",
+                    help="skip the ragged-batch step")
+    ap.add_argument("--ragged-only", action="store_true",
+                    help="only the ragged-batch step; print its figures")
     ap.add_argument("--no-stack", action="store_true",
                     help="skip the 32-layer LLaMA-7B-shaped stack decode")
     ap.add_argument("--stack-only", action="store_true",
@@ -553,6 +625,9 @@ def main():
         return
     if args.stack_only:
         print(json.dumps(llama_stack_decode()), flush=True)
+        return
+    if args.ragged_only:
+        print(json.dumps(ragged_step()), flush=True)
         return
 
     from kv_cache_eviction_03_amd import H2OCache
@@ -720,6 +795,8 @@ def main():
         dense = dense_comparator(w)
         dense["h2o_decode_speedup"] = dense["decode_us_per_step"] / dec_kernel_us
         result["dense_comparator"] = dense
+    if not args.no_ragged:
+        result["ragged_step"] = ragged_step()
     if not args.no_stack:
         result["llama_stack_decode"] = llama_stack_decode()
     if not args.no_stream:

@@ -129,9 +129,10 @@ class H2OCache:
         return out, colsum
 
     def decode_ragged(self, q, k_new, v_new, out=None, victim_slot=None, evicted_pos=None,
-                      evicted_acc=None):
+                      evicted_acc=None, t=None):
         """One token per sequence at its own position t_seq[b] (device int32 [B]); advances
-        every t_seq[b] by one. Returns out [B, H, d] fp32."""
+        every t_seq[b] by one. With t (device int32 [B]) given, the positions are taken from
+        it instead and t_seq is left alone. Returns out [B, H, d] fp32."""
         shape = (self.batch, self.heads, self.head_dim)
         for x, name in ((q, "q"), (k_new, "k_new"), (v_new, "v_new")):
             self._check(x, shape, name)
@@ -141,11 +142,16 @@ class H2OCache:
         if victim_slot is not None or evicted_pos is not None or evicted_acc is not None:
             aux = DecodeAux(_ptr(victim_slot), _ptr(evicted_pos), _ptr(evicted_acc))
         ws = self.workspace
-        check(h2o_decode_step_ragged(self.desc(), self.t_seq.data_ptr(), q.data_ptr(),
+        tp = self.t_seq if t is None else t
+        if tp.dtype != torch.int32 or tuple(tp.shape) != (self.batch,) or not tp.is_contiguous() \
+                or tp.device != self.device:
+            raise ValueError(f"t: expected contiguous int32 ({self.batch},) on {self.device}")
+        check(h2o_decode_step_ragged(self.desc(), tp.data_ptr(), q.data_ptr(),
                                      k_new.data_ptr(), v_new.data_ptr(), out.data_ptr(), aux,
                                      ws.data_ptr(), ws.numel(), _stream(self.device)),
               "h2o_decode_step_ragged")
-        self.t_seq += 1
+        if t is None:
+            self.t_seq += 1
         return out
 
     def state(self) -> dict:
