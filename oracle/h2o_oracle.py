@@ -53,6 +53,24 @@ justification in the design notes of the repository):
       layer decides independently).
   R12 k_local >= 1, so the new token is never a candidate.
 
+Eviction policies. The baselines and comparisons the pages name ([blog] §3.1.1:
+Local, Strided sparse attention, Top-K by current attention; §3.3 Q1: StreamLLM's
+sinks plus window; §3.3 Q4: heavy-only and local-only) run on the same slots with
+a different ranking. Seeding keeps the last k_local positions plus the top k_heavy
+of the rest by (seed score desc, position desc); a decode step evicts, among the
+candidates (pos <= t - k_local), the minimum of (key, position):
+  "h2o"      seed score c_j (the column sum), key = acc (the running score);
+  "sinks"    seed score [j < n_sink], key = [pos < n_sink]: with k_heavy = n_sink
+             the cache holds the first n_sink tokens and the most recent window;
+  "strided"  seed score [j % s == 0], key = [pos % s == 0]: the window plus the
+             most recent multiples of the stride s;
+  "topk"     key = this step's probability p of the slot (the token with the
+             least attention now goes); its seeding uses c_j (R13).
+Local is "h2o" with k_heavy = 0, heavy-only is k_local = 1. The running score acc
+is kept under every policy.
+  R13 The pages give Top-K no prompt-time score; the column sum (the same
+      cumulative attention H2O seeds with) is used.
+
 Near-tie adoption (the tolerance rule): when an accelerator implementation made
 a different choice whose score lies within `rel_tol` (relative) of the oracle's
 own choice, the oracle may adopt that choice so that the two states stay
@@ -96,13 +114,29 @@ def column_sums(P: np.ndarray) -> np.ndarray:
     return P.sum(axis=0)
 
 
+POLICIES = ("h2o", "sinks", "strided", "topk")
+
+
+def policy_seed_scores(policy: str, param: int, c32: np.ndarray) -> np.ndarray:
+    """The fp32 score each prompt position is ranked by at seeding (see the header)."""
+    j = np.arange(len(c32))
+    if policy in ("h2o", "topk"):
+        return np.asarray(c32, dtype=np.float32)
+    if policy == "sinks":
+        return (j < param).astype(np.float32)
+    if policy == "strided":
+        return (j % param == 0).astype(np.float32)
+    raise ValueError(f"unknown policy {policy!r}")
+
+
 def seed_positions(c32: np.ndarray, k_heavy: int, k_local: int) -> list[int]:
     """Positions kept after a prompt of length T = len(c32).
 
     If T <= k every position is kept. Otherwise the last k_local positions are
     kept ([blog] §2.2 recent tokens) plus the k_heavy highest-scoring of the
     remaining ones ([analysis] §3.1 top-k of cumulative attention), ranked by
-    (score desc, position desc) on the fp32 scores (R7, R10).
+    (score desc, position desc) on the fp32 scores (R7, R10). Under another
+    policy c32 holds that policy's seed scores.
     """
     T = len(c32)
     k = k_heavy + k_local
@@ -124,6 +158,8 @@ class UnitCache:
     k_heavy: int
     k_local: int
     head_dim: int
+    policy: str = "h2o"                      # eviction ranking (see the header)
+    policy_param: int = 0                    # n_sink ("sinks") or the stride ("strided")
     pos: np.ndarray = field(init=False)      # [k] int64, FREE = -1
     K: np.ndarray = field(init=False)        # [k, d] float64 (exact stored values)
     V: np.ndarray = field(init=False)
@@ -137,6 +173,11 @@ class UnitCache:
     def __post_init__(self):
         if self.k_local < 1 or self.k_heavy < 0:
             raise ValueError("need k_local >= 1 and k_heavy >= 0 (R12)")
+        if self.policy not in POLICIES:
+            raise ValueError(f"unknown policy {self.policy!r}")
+        if (self.policy == "sinks" and self.policy_param < 0) or \
+                (self.policy == "strided" and self.policy_param < 1):
+            raise ValueError(f"bad parameter {self.policy_param} for policy {self.policy!r}")
         k = self.k
         self.pos = np.full(k, FREE, dtype=np.int64)
         self.K = np.zeros((k, self.head_dim))
@@ -178,7 +219,8 @@ def prefill(cache: UnitCache, Q, K, V, adopt_kept=None, rel_tol=1e-5):
     O = P @ V
     c64 = column_sums(P)
     c32 = c64.astype(np.float32)
-    kept = seed_positions(c32, cache.k_heavy, cache.k_local)
+    score = policy_seed_scores(cache.policy, cache.policy_param, c32)
+    kept = seed_positions(score, cache.k_heavy, cache.k_local)
 
     if adopt_kept is not None:
         other = sorted(int(p) for p in adopt_kept)
@@ -188,7 +230,7 @@ def prefill(cache: UnitCache, Q, K, V, adopt_kept=None, rel_tol=1e-5):
             local = set(range(max(0, T - cache.k_local), T))
             ok = (len(other) == len(kept) and not (local - set(other))
                   and all(0 <= p < T for p in other)
-                  and all(_near(float(c32[x]), float(c32[y]), rel_tol)
+                  and all(_near(float(score[x]), float(score[y]), rel_tol)
                           for x in theirs for y in ours))
             if not ok:
                 raise ParityError(f"prefill kept sets differ beyond a near tie: "
@@ -209,6 +251,17 @@ def prefill(cache: UnitCache, Q, K, V, adopt_kept=None, rel_tol=1e-5):
         cache.evictions.append((T - 1, FREE, p, c32[p]))
     cache.rows += T
     return O, c64
+
+
+def _decode_keys(cache: UnitCache, p32: np.ndarray) -> np.ndarray:
+    """Per slot, the fp32 value a decode step ranks eviction candidates by (header)."""
+    if cache.policy == "h2o":
+        return cache.acc.copy()
+    if cache.policy == "topk":
+        return np.asarray(p32, dtype=np.float32)
+    if cache.policy == "sinks":
+        return (cache.pos < cache.policy_param).astype(np.float32)
+    return (cache.pos % cache.policy_param == 0).astype(np.float32)
 
 
 def decode(cache: UnitCache, t: int, q, k_new, v_new, adopt_victim=None,
@@ -255,17 +308,17 @@ def decode(cache: UnitCache, t: int, q, k_new, v_new, adopt_victim=None,
     else:
         limit = t - cache.k_local
         cand = [s_ for s_ in range(cache.k) if cache.pos[s_] <= limit]
-        victim = min(cand, key=lambda s_: (float(cache.acc[s_]), int(cache.pos[s_])))
+        key = _decode_keys(cache, p32[:n])
+        victim = min(cand, key=lambda s_: (float(key[s_]), int(cache.pos[s_])))
         if adopt_victim is not None and int(adopt_victim) != victim:
             g = int(adopt_victim)
-            if g not in cand or not _near(float(cache.acc[g]), float(cache.acc[victim]),
-                                          rel_tol):
+            if g not in cand or not _near(float(key[g]), float(key[victim]), rel_tol):
                 raise ParityError(
                     f"t={t}: victim slot {g} (pos {int(cache.pos[g]) if 0 <= g < cache.k else None}) "
                     f"is not a near tie with the oracle's slot {victim} "
-                    f"(pos {int(cache.pos[victim])}, score {float(cache.acc[victim])!r})")
+                    f"(pos {int(cache.pos[victim])}, key {float(key[victim])!r})")
             cache.ties.append(("decode", t, int(cache.pos[g]), int(cache.pos[victim]),
-                               float(cache.acc[g]), float(cache.acc[victim])))
+                               float(key[g]), float(key[victim])))
             victim = g
         slot = victim
         cache.evictions.append((t, slot, int(cache.pos[slot]), cache.acc[slot]))

@@ -324,3 +324,88 @@ def test_brute_force_replay_exact_uniform(T, n, kh, kl):
                                rtol=0, atol=1e-12)
     for p in range(N):
         assert abs(cache.hist64[p] - float(bf["scores"][p])) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# Eviction policies other than H2O ([blog] §3.1.1 baselines, §3.3 Q1 StreamLLM)
+# ---------------------------------------------------------------------------
+
+def _policy_run(policy, param, kh, kl, T, n, d=16, seed=0):
+    rng = np.random.default_rng(seed)
+    N = T + n
+    Q, K, V = (rng.standard_normal((N, d)) for _ in range(3))
+    cache = UnitCache(kh, kl, d, policy=policy, policy_param=param)
+    prefill(cache, Q[:T], K[:T], V[:T])
+    kept = [cache.kept_positions()]
+    for i in range(n):
+        decode(cache, T + i, Q[T + i], K[T + i], V[T + i])
+        kept.append(cache.kept_positions())
+    return kept
+
+
+@pytest.mark.parametrize("n_sink,kl,T", [(4, 8, 40), (1, 3, 10), (0, 5, 12)])
+def test_sinks_policy_keeps_first_tokens_and_window(n_sink, kl, T):
+    # StreamLLM's cache: the first n_sink tokens plus the most recent window. With
+    # k_heavy = n_sink that is the whole budget, after the prompt and after every step.
+    kept = _policy_run("sinks", n_sink, n_sink, kl, T, n=30)
+    for i, ks in enumerate(kept):
+        last = T - 1 + i
+        assert ks == sorted(set(range(n_sink)) | set(range(last - kl + 1, last + 1)))
+
+
+@pytest.mark.parametrize("s,kh,kl,T", [(4, 5, 6, 60), (3, 2, 1, 20), (7, 3, 4, 90)])
+def test_strided_policy_keeps_window_and_latest_multiples(s, kh, kl, T):
+    # Strided retention: the window plus the k_heavy most recent multiples of the stride
+    # among the older positions (enough of them exist in these cases).
+    kept = _policy_run("strided", s, kh, kl, T, n=40)
+    for i, ks in enumerate(kept):
+        last = T - 1 + i
+        older = [p for p in range(last - kl + 1) if p % s == 0]
+        assert ks == sorted(set(older[-kh:]) | set(range(last - kl + 1, last + 1)))
+
+
+def test_position_policies_ignore_the_values():
+    # Under a position-only ranking the kept sets cannot depend on Q/K/V.
+    for policy, param in (("sinks", 3), ("strided", 5)):
+        a = _policy_run(policy, param, 3, 4, 30, 20, seed=1)
+        b = _policy_run(policy, param, 3, 4, 30, 20, seed=2)
+        assert a == b
+
+
+def test_topk_policy_evicts_the_least_attended_now():
+    # Keys along the query: logit_j = a_j / sqrt(d), so this step's attention order is the
+    # order of a_j by construction (no softmax needed). Slots hold positions 0..4 with
+    # a = [3, 1, 4, 1, 5]; k_local = 2 protects positions 4 and the new token 5. The
+    # candidates are positions 0..3; the least attended have a = 1 (positions 1 and 3),
+    # and the tie goes to the older one: position 1 leaves, whatever the running scores.
+    d = 8
+    q = np.zeros(d)
+    q[0] = 1.0
+    a = [3.0, 1.0, 4.0, 1.0, 5.0]
+    cache = UnitCache(3, 2, d, policy="topk")
+    for slot, (pos, ai) in enumerate(zip(range(5), a)):
+        cache.pos[slot] = pos
+        cache.K[slot] = ai * q
+        cache.V[slot] = 0.0
+        cache.acc[slot] = np.float32([0.1, 9.0, 0.2, 9.0, 0.3][slot])   # H2O would pick pos 0
+        cache.hist32[pos], cache.hist64[pos] = cache.acc[slot], float(cache.acc[slot])
+    _, victim = decode(cache, 5, q, 2.0 * q, np.zeros(d))
+    assert victim == 1 and cache.kept_positions() == [0, 2, 3, 4, 5]
+    # the same state under H2O evicts the lowest running score instead (position 0)
+    cache2 = UnitCache(3, 2, d)
+    for slot in range(5):
+        cache2.pos[slot], cache2.K[slot], cache2.acc[slot] = cache.pos[slot], a[slot] * q, \
+            np.float32([0.1, 9.0, 0.2, 9.0, 0.3][slot])
+        cache2.pos[slot] = slot
+        cache2.hist32[slot], cache2.hist64[slot] = cache2.acc[slot], float(cache2.acc[slot])
+    _, v2 = decode(cache2, 5, q, 2.0 * q, np.zeros(d))
+    assert v2 == 0
+
+
+def test_policy_parameters_are_checked():
+    with pytest.raises(ValueError):
+        UnitCache(2, 2, 8, policy="strided", policy_param=0)
+    with pytest.raises(ValueError):
+        UnitCache(2, 2, 8, policy="sinks", policy_param=-1)
+    with pytest.raises(ValueError):
+        UnitCache(2, 2, 8, policy="lru")
