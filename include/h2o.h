@@ -61,6 +61,34 @@ typedef enum {
 
 typedef enum { H2O_F32 = 0, H2O_F16 = 1, H2O_BF16 = 2 } h2o_dtype;
 
+/*
+ * Eviction ranking. Seeding keeps the last k_local prompt positions plus the
+ * k_heavy others ranked highest by (seed score, position); a decode step with a
+ * full cache evicts, among slots with slot_pos <= t - k_local, the smallest
+ * (key, slot_pos), compared lexicographically.
+ *   H2O_POLICY_H2O      seed score: column sum c_j; key: acc_score (H2O blog
+ *                       §2.2; analysis page §3.1, §3.2)
+ *   H2O_POLICY_SINKS    seed score: 1 for positions < policy_param, else 0; key
+ *                       likewise: the first policy_param tokens stay (with
+ *                       k_heavy = policy_param the cache is those sinks plus the
+ *                       most recent window, the StreamLLM comparison of the blog
+ *                       §3.3 Q1); policy_param >= 0
+ *   H2O_POLICY_STRIDED  seed score and key: 1 for positions that are multiples
+ *                       of policy_param, else 0 (blog §3.1.1 "Strided"):
+ *                       the window plus the latest multiples; policy_param >= 1
+ *   H2O_POLICY_TOPK     seed score: c_j; key: the slot's attention probability
+ *                       in this step (blog §3.1.1 "Top-K": the token attended
+ *                       least now leaves)
+ * acc_score accumulates every step under every policy. Local is H2O with
+ * k_heavy = 0; heavy-only is k_local = 1.
+ */
+typedef enum {
+  H2O_POLICY_H2O = 0,
+  H2O_POLICY_SINKS = 1,
+  H2O_POLICY_STRIDED = 2,
+  H2O_POLICY_TOPK = 3
+} h2o_policy;
+
 /* Limits of this build. */
 #define H2O_MAX_SLOTS 8192        /* k = k_heavy + k_local */
 #define H2O_MAX_POSITION 0x7fffffff
@@ -77,6 +105,7 @@ typedef enum { H2O_F32 = 0, H2O_F16 = 1, H2O_BF16 = 2 } h2o_dtype;
  *   k_slots, v_slots  16-byte aligned
  *   slot_pos      int32 absolute position held by each slot, -1 = free
  *   acc_score     fp32 accumulated attention score of each slot
+ *   policy, policy_param  eviction ranking (h2o_policy above); 0, 0 is H2O
  * Valid slots always form a prefix [0, n_valid) of each unit's slots.
  */
 typedef struct {
@@ -90,6 +119,8 @@ typedef struct {
   void* v_slots;
   int32_t* slot_pos;
   float* acc_score;
+  int32_t policy;
+  int32_t policy_param;
 } h2o_cache_desc;
 
 /*

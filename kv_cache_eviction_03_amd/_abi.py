@@ -15,6 +15,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libh2o.so")
 
 H2O_OK, H2O_ERR_INVALID, H2O_ERR_UNSUPPORTED, H2O_ERR_WORKSPACE, H2O_ERR_HIP = range(5)
 H2O_F32, H2O_F16, H2O_BF16 = range(3)
+H2O_POLICY_H2O, H2O_POLICY_SINKS, H2O_POLICY_STRIDED, H2O_POLICY_TOPK = range(4)
+POLICY_CODES = {"h2o": H2O_POLICY_H2O, "sinks": H2O_POLICY_SINKS,
+                "strided": H2O_POLICY_STRIDED, "topk": H2O_POLICY_TOPK}
 H2O_MAX_SLOTS = 8192
 
 EXPORTS = ("h2o_reset", "h2o_workspace_bytes", "h2o_prefill", "h2o_decode_step",
@@ -26,7 +29,8 @@ class CacheDesc(ctypes.Structure):
     _fields_ = [("batch", c_int32), ("heads", c_int32), ("head_dim", c_int32),
                 ("k_heavy", c_int32), ("k_local", c_int32), ("dtype", c_int32),
                 ("k_slots", c_void_p), ("v_slots", c_void_p),
-                ("slot_pos", c_void_p), ("acc_score", c_void_p)]
+                ("slot_pos", c_void_p), ("acc_score", c_void_p),
+                ("policy", c_int32), ("policy_param", c_int32)]
 
 
 class DecodeAux(ctypes.Structure):

@@ -8,7 +8,8 @@ from __future__ import annotations
 
 import torch
 
-from ._abi import (H2O_BF16, H2O_F16, H2O_F32, CacheDesc, DecodeAux, check, h2o_decode_step,
+from ._abi import (H2O_BF16, H2O_F16, H2O_F32, POLICY_CODES, CacheDesc, DecodeAux, check,
+                   h2o_decode_step,
                    h2o_decode_step_ragged, h2o_prefill, h2o_prefill_ragged, h2o_reset,
                    h2o_workspace_bytes)
 
@@ -24,12 +25,17 @@ def _ptr(x: torch.Tensor | None) -> int:
 
 
 class H2OCache:
-    """k = k_heavy + k_local slots per (sequence, head) of one layer."""
+    """k = k_heavy + k_local slots per (sequence, head) of one layer; `policy` picks the
+    eviction ranking (h2o, sinks, strided, topk; see include/h2o.h)."""
 
     def __init__(self, batch: int, heads: int, head_dim: int, k_heavy: int, k_local: int,
-                 dtype: torch.dtype, device="cuda", max_prompt: int = 0):
+                 dtype: torch.dtype, device="cuda", max_prompt: int = 0, policy: str = "h2o",
+                 policy_param: int = 0):
         if dtype not in _DTYPE_CODE:
             raise ValueError(f"unsupported dtype {dtype}")
+        if policy not in POLICY_CODES:
+            raise ValueError(f"unknown policy {policy!r}")
+        self.policy, self.policy_param = policy, policy_param
         self.batch, self.heads, self.head_dim = batch, heads, head_dim
         self.k_heavy, self.k_local = k_heavy, k_local
         self.k = k_heavy + k_local
@@ -53,7 +59,8 @@ class H2OCache:
         return CacheDesc(self.batch, self.heads, self.head_dim, self.k_heavy, self.k_local,
                          _DTYPE_CODE[self.dtype], self.k_slots.data_ptr(),
                          self.v_slots.data_ptr(), self.slot_pos.data_ptr(),
-                         self.acc_score.data_ptr())
+                         self.acc_score.data_ptr(), POLICY_CODES[self.policy],
+                         self.policy_param)
 
     def reserve(self, max_prompt: int) -> None:
         need = h2o_workspace_bytes(self.desc(), max_prompt)

@@ -239,9 +239,11 @@ void decode_resident_kernel(DecodeParams p) {
   uint64_t key = ~0ull;
   float a = 0.f;
   if (own) {
-    a = acc_old + fast_exp2(lg_own - M) * inv;
+    const float pj = fast_exp2(lg_own - M) * inv;
+    a = acc_old + pj;
     acc[jo] = a;
-    if (full && pos_old <= limit) key = score_key(a, pos_old);
+    if (full && pos_old <= limit)
+      key = score_key(policy_key(p.policy, p.policy_param, a, pj, pos_old), pos_old);
   }
   const uint64_t wmin = wave_min_u64_uniform(key);
   if (lane == 0) s_key[wave] = wmin;
@@ -438,13 +440,15 @@ __global__ __launch_bounds__(kCombThreads) void decode_split_combine_kernel(Deco
   // scores: slot j = tid + i * kCombThreads
   uint64_t best = ~0ull;
   int best_slot = -1;
+  float best_acc = 0.f;
   auto score = [&](int j, float lgv, float acv, int psv) {
     if (j < n) {
-      const float a = acv + fast_exp2(lgv - M) * inv;
+      const float pj = fast_exp2(lgv - M) * inv;
+      const float a = acv + pj;
       acc[j] = a;
       if (full && psv <= limit) {
-        const uint64_t key = score_key(a, psv);
-        if (key < best) { best = key; best_slot = j; }
+        const uint64_t key = score_key(policy_key(p.policy, p.policy_param, a, pj, psv), psv);
+        if (key < best) { best = key; best_slot = j; best_acc = a; }
       }
     }
   };
@@ -483,13 +487,13 @@ __global__ __launch_bounds__(kCombThreads) void decode_split_combine_kernel(Deco
     if (tid == dst % kCombThreads) {            // visited slot dst in the score loop
       pos[dst] = t;
       acc[dst] = fast_exp2(lg_new - M) * inv;
+      if (full && p.evicted_acc) p.evicted_acc[unit] = best_acc;   // the victim's final score
     }
   }
   if (tid == 0) {
     if (p.victim_slot) p.victim_slot[unit] = full ? dst : -1;
     if (p.evicted_pos) p.evicted_pos[unit] = full && dst >= 0 ? (int32_t)(uint32_t)gbest : -1;
-    if (p.evicted_acc)
-      p.evicted_acc[unit] = full && dst >= 0 ? __uint_as_float((uint32_t)(gbest >> 32)) : 0.f;
+    if (p.evicted_acc && !(full && dst >= 0)) p.evicted_acc[unit] = 0.f;
   }
 }
 

@@ -50,6 +50,12 @@ h2o_status check_desc(const h2o_cache_desc* c) {
   if (c->k_local < 1)
     return fail(H2O_ERR_INVALID, "k_local %d < 1: the new token must stay in the recent window",
                 c->k_local);
+  if (c->policy < H2O_POLICY_H2O || c->policy > H2O_POLICY_TOPK)
+    return fail(H2O_ERR_INVALID, "policy %d is not an h2o_policy", c->policy);
+  if ((c->policy == H2O_POLICY_SINKS && c->policy_param < 0) ||
+      (c->policy == H2O_POLICY_STRIDED && c->policy_param < 1))
+    return fail(H2O_ERR_INVALID, "policy_param %d out of range for policy %d", c->policy_param,
+                c->policy);
   if ((int64_t)c->k_heavy + c->k_local > H2O_MAX_SLOTS)
     return fail(H2O_ERR_UNSUPPORTED, "k = %lld exceeds H2O_MAX_SLOTS (%d)",
                 (long long)c->k_heavy + c->k_local, H2O_MAX_SLOTS);
@@ -184,7 +190,7 @@ h2o_status prefill_impl(const h2o_cache_desc* c, const void* q, const void* k, c
   }
   h2o::SeedParams sp{k, v, colpart, colsum, lens, c->k_slots, c->v_slots, c->slot_pos,
                      c->acc_score, (int32_t)units, c->heads, T, part_rows_of(c, T), c->k_heavy,
-                     c->k_local};
+                     c->k_local, c->policy, c->policy_param};
   if ((e = h2o::launch_seed(dt, D, sp, s))) return hip_fail(e, "seed launch");
   return H2O_OK;
 }
@@ -226,7 +232,8 @@ h2o_status decode_impl(const h2o_cache_desc* c, int64_t t, const int32_t* tpos, 
               : h2o::SplitScratch{};
   h2o::DecodeParams p{q, k_new, v_new, c->k_slots, c->v_slots, c->slot_pos, c->acc_score, out,
                       aux ? aux->victim_slot : nullptr, aux ? aux->evicted_pos : nullptr,
-                      aux ? aux->evicted_acc : nullptr, tpos, (int32_t)(c->batch * c->heads),
+                      aux ? aux->evicted_acc : nullptr, tpos, c->policy, c->policy_param,
+                      (int32_t)(c->batch * c->heads),
                       c->heads, kk, c->k_local, (int32_t)t, qk_scale(D)};
   if (hipError_t e = h2o::launch_decode(dtype_of(c), D, p, w, static_cast<hipStream_t>(stream)))
     return hip_fail(e, "decode launch");

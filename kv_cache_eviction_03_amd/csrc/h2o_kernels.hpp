@@ -53,6 +53,8 @@ struct DecodeParams {
   int32_t* evicted_pos; // [units] or null
   float* evicted_acc;   // [units] or null
   const int32_t* tpos;  // [batch] per-sequence positions (device), or null: t for all
+  int32_t policy;       // eviction ranking, h2o_policy
+  int32_t policy_param;
   int32_t units;
   int32_t heads;        // units of one sequence
   int32_t k;
@@ -60,6 +62,24 @@ struct DecodeParams {
   int32_t t;
   float qk_scale;       // log2(e) / sqrt(D): logits are kept in the log2 domain
 };
+
+// Eviction rankings (the C ABI's h2o_policy). The fp32 value a candidate is ranked by:
+// the running score (H2O), this step's probability (Top-K), or a 0/1 position class
+// (sinks: 1 below policy_param; strided: 1 on multiples of policy_param). All are >= 0, so
+// their bit patterns order like the values.
+enum : int { kPolicyH2O = 0, kPolicySinks = 1, kPolicyStrided = 2, kPolicyTopK = 3 };
+__host__ __device__ inline float policy_key(int policy, int param, float acc, float p, int pos) {
+  if (policy == kPolicyH2O) return acc;
+  if (policy == kPolicyTopK) return p;
+  if (policy == kPolicySinks) return pos < param ? 1.f : 0.f;
+  return pos % param == 0 ? 1.f : 0.f;
+}
+// The seed score of prompt position j (column sum c under H2O and Top-K).
+__host__ __device__ inline float policy_seed(int policy, int param, float c, int j) {
+  if (policy == kPolicySinks) return j < param ? 1.f : 0.f;
+  if (policy == kPolicyStrided) return j % param == 0 ? 1.f : 0.f;
+  return c;
+}
 
 // A unit's own bound from a per-sequence device array (clamped to [0, hi], so a bad entry
 // cannot address outside the buffers), or the shared value when there is no array.
@@ -114,6 +134,8 @@ struct SeedParams {
   int32_t part_rows;    // query rows per partial row
   int32_t k_heavy;
   int32_t k_local;
+  int32_t policy;       // seeding ranking, h2o_policy
+  int32_t policy_param;
 };
 
 struct ResetParams {

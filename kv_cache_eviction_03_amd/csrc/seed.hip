@@ -3,7 +3,8 @@
 // seed: per unit, keep the last k_local prompt positions (the recent tokens of
 // the H2O blog, ttsmallhot.github.io, §2.2) plus the k_heavy positions of
 // [0, T - k_local) with the highest fp32 column sum, i.e. the top-k of the
-// cumulative attention ("H2O Heavy-Hitter Oracle 分析", §3.1). Ties rank the
+// cumulative attention ("H2O Heavy-Hitter Oracle 分析", §3.1) — or, under a
+// position policy (blog §3.1.1, §3.3 Q1), the highest 0/1 position class. Ties rank the
 // newer position higher, so the older one is dropped. If T <= k every
 // position is kept. Kept positions fill slots 0.. in ascending order; the
 // other slots are marked free.
@@ -152,7 +153,12 @@ __global__ __launch_bounds__(kThreads) void seed_kernel(SeedParams p) {
     for (int s = tid; s < T_; s += kThreads) slot_of[s] = s;
   } else {
     const int ncand = T_ - p.k_local;
-    auto key = [&](int j) -> unsigned { return staged ? bits[j] : __float_as_uint(c[j]); };
+    // The ranking score of position j: the column sum under H2O and Top-K, a 0/1 position
+    // class under the position policies.
+    auto key = [&](int j) -> unsigned {
+      const float cj = staged ? __uint_as_float(bits[j]) : c[j];
+      return __float_as_uint(policy_seed(p.policy, p.policy_param, cj, j));
+    };
 
     unsigned prefix = 0, mask = 0, want = (unsigned)p.k_heavy, eq_total = 0;
     if (p.k_heavy > 0) {

@@ -31,7 +31,8 @@ def run_gpu(w, x, record_steps=True):
 
     B, H, d, T, n = w.batch, w.heads, w.head_dim, w.prompt, w.steps
     dev = x["q_dec"].device if n else x["q_prompt"].device
-    cache = H2OCache(B, H, d, w.k_heavy, w.k_local, w.torch_dtype, dev, max_prompt=T)
+    cache = H2OCache(B, H, d, w.k_heavy, w.k_local, w.torch_dtype, dev, max_prompt=T,
+                     policy=w.policy, policy_param=w.policy_param)
     cache.reset()
     r = {}
     if T > 0:
@@ -62,7 +63,8 @@ def run_gpu_ragged(w, x, lens):
 
     B, H, d, T, n = w.batch, w.heads, w.head_dim, w.prompt, w.steps
     dev = x["q_prompt"].device
-    cache = H2OCache(B, H, d, w.k_heavy, w.k_local, w.torch_dtype, dev, max_prompt=T)
+    cache = H2OCache(B, H, d, w.k_heavy, w.k_local, w.torch_dtype, dev, max_prompt=T,
+                     policy=w.policy, policy_param=w.policy_param)
     cache.reset()
     lens_d = torch.tensor(lens, dtype=torch.int32, device=dev)
     r = {}
@@ -135,7 +137,8 @@ def check_unit(w, x, r, b, h, steps=None, prompt_len=None):
     u["Qp"], u["Kp"], u["Vp"] = u["Qp"][:T], u["Kp"][:T], u["Vp"][:T]
     pos0 = r["pos0"][b, h].cpu().numpy()
     acc0 = r["acc0"][b, h].cpu().numpy()
-    cache = UnitCache(w.k_heavy, w.k_local, w.head_dim)
+    cache = UnitCache(w.k_heavy, w.k_local, w.head_dim, policy=w.policy,
+                      policy_param=w.policy_param)
     err = {"prefill_out": 0.0, "decode_out": 0.0, "colsum_rel": 0.0, "acc_rel": 0.0}
     if T > 0:
         kept_gpu = sorted(int(p) for p in pos0 if p >= 0)

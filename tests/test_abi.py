@@ -76,6 +76,10 @@ def test_workspace_bytes():
     (dict(acc_score=0), h2o.H2O_ERR_INVALID),
     (dict(v_slots=A + 8), h2o.H2O_ERR_INVALID),
     (dict(slot_pos=A + 2), h2o.H2O_ERR_INVALID),
+    (dict(policy=4), h2o.H2O_ERR_INVALID),
+    (dict(policy=-1), h2o.H2O_ERR_INVALID),
+    (dict(policy=2, policy_param=0), h2o.H2O_ERR_INVALID),
+    (dict(policy=1, policy_param=-1), h2o.H2O_ERR_INVALID),
 ])
 def test_descriptor_checks(kw, status):
     d = desc(**kw)

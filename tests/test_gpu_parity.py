@@ -135,6 +135,33 @@ def test_ragged_batch(dtype, d):
              f"ties={len(agg['ties'])}")
 
 
+POLICY_CASES = [
+    # sinks + window (k_heavy = n_sink = 4), resident decode
+    Workload(83, "policy-sinks-f16", 2, 1, 3, 128, "f16", 200, 40, 4, 28, heavy_frac=0.05,
+             policy="sinks", policy_param=4),
+    # strided (stride 8), resident decode
+    Workload(82, "policy-strided-f16", 2, 1, 3, 128, "f16", 200, 40, 12, 20, policy="strided",
+             policy_param=8),
+    # Top-K by this step's attention, bf16 d=64
+    Workload(81, "policy-topk-bf16-d64", 2, 1, 3, 64, "bf16", 200, 40, 24, 16,
+             heavy_frac=0.05, policy="topk"),
+    # the split decode (k = 300, fp32 d=128) under Top-K and under sinks
+    Workload(80, "policy-topk-split-f32", 1, 1, 2, 128, "f32", 280, 30, 150, 150, policy="topk"),
+    Workload(79, "policy-sinks-split-bf16", 1, 1, 2, 128, "bf16", 400, 30, 8, 292,
+             policy="sinks", policy_param=8),
+]
+
+
+@pytest.mark.parametrize("w", POLICY_CASES, ids=[w.name for w in POLICY_CASES])
+def test_eviction_policies(w):
+    announce(f"[parity] {w.name}: policy {w.policy}({w.policy_param}), k = {w.k_heavy}+{w.k_local}")
+    x = gen(w)
+    r = run_gpu(w, x)
+    agg = check_units(w, x, r, range(w.units_per_layer))
+    announce(f"[parity] {w.name}: prefill {agg['prefill_out']:.2e} decode {agg['decode_out']:.2e} "
+             f"ties={len(agg['ties'])}")
+
+
 def test_llama7b_layer_bf16_sampled_units():
     w = WORKLOADS[3]
     for layer in (0, 31):

@@ -51,6 +51,8 @@ class Workload:
     k_local: int
     heavy_frac: float = 0.0
     sinks: int = 0
+    policy: str = "h2o"       # eviction ranking the cache runs with (h2o, sinks, strided, topk)
+    policy_param: int = 0
 
     @property
     def k(self) -> int:
