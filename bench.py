@@ -32,6 +32,7 @@ Timing:
   * hbm_measured_ceiling: context only, plain PyTorch streaming read and copy rates;
   * ragged_step: the bench layer with seeded prompt lengths in [256, 512] through the
     ragged entry points, against the same batch padded to 512;
+  * decode_by_policy: the bench layer's decode launch under each eviction ranking;
   * llama_stack_decode: the LLaMA-7B-shaped model's decode step, 32 layers each with
     its own prefilled cache (3.69 GB of slots per step, far beyond the MALL);
   * stream_sustained: the long-streaming workload in full (4096 slots, 2^20 decode
@@ -129,6 +130,50 @@ def prefill_mfma_probe(reps=10, warmup=3):
            "note": "algorithmic flops 2T(T+1)d per unit over one h2o_prefill call "
                    "(attention + column sums + seeding)"}
     del x, c, out, cs
+    torch.cuda.empty_cache()
+    return res
+
+
+def decode_by_policy(n=32, reps=5):
+    """The bench layer's decode launch under each eviction ranking (H2O, sinks + window,
+    strided, Top-K by current attention), graph-replayed like decode_by_workload; context:
+    the ranking changes one fp32 value per candidate, not the bytes moved."""
+    import torch
+
+    from kv_cache_eviction_03_amd import H2OCache
+    from workloads import WORKLOADS, generate
+    dev = "cuda:0"
+    w = WORKLOADS[2].scaled(steps=n)
+    x = generate(w, seed=0, device=dev)
+    out = torch.empty((n, w.batch, w.heads, w.head_dim), dtype=torch.float32, device=dev)
+    res = []
+    for policy, param in (("h2o", 0), ("sinks", 4), ("strided", 8), ("topk", 0)):
+        c = H2OCache(w.batch, w.heads, w.head_dim, w.k_heavy, w.k_local, w.torch_dtype, dev,
+                     max_prompt=w.prompt, policy=policy, policy_param=param)
+        c.reset()
+        c.prefill(x["q_prompt"], x["k_prompt"], x["v_prompt"])
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream(dev)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for i in range(n):
+                    c.decode(x["q_dec"][i], x["k_dec"][i], x["v_dec"][i], out=out[i])
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(reps):
+            c.reset()
+            c.prefill(x["q_prompt"], x["k_prompt"], x["v_prompt"])
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            us = 1e3 * a.elapsed_time(b) / n
+            best = us if best is None else min(best, us)
+        res.append({"policy": policy, "policy_param": param, "us_per_launch": best})
+        del c, g
+    del x, out
     torch.cuda.empty_cache()
     return res
 
@@ -628,6 +673,7 @@ def main():
         return
     if args.ragged_only:
         print(json.dumps(ragged_step()), flush=True)
+        print(json.dumps(decode_by_policy()), flush=True)
         return
 
     from kv_cache_eviction_03_amd import H2OCache
@@ -797,6 +843,7 @@ def main():
         result["dense_comparator"] = dense
     if not args.no_ragged:
         result["ragged_step"] = ragged_step()
+        result["decode_by_policy"] = decode_by_policy()
     if not args.no_stack:
         result["llama_stack_decode"] = llama_stack_decode()
     if not args.no_stream:
