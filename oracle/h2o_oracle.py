@@ -71,6 +71,16 @@ is kept under every policy.
   R13 The pages give Top-K no prompt-time score; the column sum (the same
       cumulative attention H2O seeds with) is used.
 
+Quantised slots. [blog] §3.3 Q3 reports that H2O combines with KV quantisation
+but names no scheme. With slot_format "e4m3" every K/V row that enters a slot
+is stored as OCP FP8 E4M3 codes (R14); prefill attention still reads the
+prompt's own K/V.
+  R14 One scale per cache for K and one for V (k_scale, v_scale > 0). A row x is
+      stored as codes e4m3(fl32(x * fl32(1 / scale))), rounded to nearest, ties
+      to even, saturated at +-448; it is read back as code value * scale. The new
+      token's K/V are quantised when they join, before the step's attention, so
+      the step attends to exactly what the cache then holds.
+
 Near-tie adoption (the tolerance rule): when an accelerator implementation made
 a different choice whose score lies within `rel_tol` (relative) of the oracle's
 own choice, the oracle may adopt that choice so that the two states stay
@@ -115,6 +125,58 @@ def column_sums(P: np.ndarray) -> np.ndarray:
 
 
 POLICIES = ("h2o", "sinks", "strided", "topk")
+SLOT_FORMATS = ("input", "e4m3")
+
+
+# ---------------------------------------------------------------------------
+# OCP FP8 E4M3 slot codes (R14). E4M3: a sign bit, 4 exponent bits with bias 7
+# and 3 mantissa bits. Exponent field 0 holds the subnormals m * 2^-9; exponent
+# field 15 with mantissa 7 is NaN (no infinities), so the largest finite value
+# is 1.75 * 2^8 = 448.
+# ---------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def e4m3_round(y) -> np.ndarray:
+    """The E4M3 value nearest each y (ties to even), saturated at +-448, as float64."""
+    y = np.clip(np.asarray(y, dtype=np.float64), -E4M3_MAX, E4M3_MAX)
+    a = np.abs(y)
+    _, e = np.frexp(a)                   # a = f * 2^e with f in [0.5, 1)
+    lead = np.maximum(e - 1, -6)         # exponent of the leading bit; subnormals share -6
+    quantum = np.ldexp(1.0, lead - 3)    # 3 mantissa bits below the leading bit
+    return np.copysign(np.rint(a / quantum) * quantum, y)
+
+
+def e4m3_encode(r) -> np.ndarray:
+    """Codes (uint8) of E4M3 values r (as e4m3_round returns them)."""
+    r = np.asarray(r, dtype=np.float64)
+    a = np.abs(r)
+    _, e = np.frexp(a)
+    normal = a >= 2.0 ** -6
+    lead = np.where(normal, e - 1, -6)
+    mant = np.where(normal, a / np.ldexp(1.0, lead - 3) - 8, a / 2.0 ** -9)
+    field = np.where(normal, lead + 7, 0)
+    code = (np.signbit(r).astype(np.int64) << 7) | (field.astype(np.int64) << 3) | \
+        mant.astype(np.int64)
+    return code.astype(np.uint8)
+
+
+def e4m3_decode(code) -> np.ndarray:
+    """float64 value of each E4M3 code (NaN for the two NaN codes)."""
+    c = np.asarray(code, dtype=np.int64)
+    sign = np.where(c >> 7, -1.0, 1.0)
+    field, mant = (c >> 3) & 15, c & 7
+    mag = np.where(field == 0, mant * 2.0 ** -9, np.ldexp(1.0 + mant / 8.0, field - 7))
+    return np.where((field == 15) & (mant == 7), np.nan, sign * mag)
+
+
+def quantize_row(x, scale):
+    """Codes and read-back values of a K or V row stored in an E4M3 slot (R14)."""
+    s32 = np.float32(scale)
+    y = np.asarray(x, dtype=np.float32) * (np.float32(1.0) / s32)   # one fp32 rounding
+    r = e4m3_round(y)
+    return e4m3_encode(r), r * float(s32)
 
 
 def policy_seed_scores(policy: str, param: int, c32: np.ndarray) -> np.ndarray:
@@ -160,9 +222,14 @@ class UnitCache:
     head_dim: int
     policy: str = "h2o"                      # eviction ranking (see the header)
     policy_param: int = 0                    # n_sink ("sinks") or the stride ("strided")
+    slot_format: str = "input"               # "input" or "e4m3" (R14)
+    k_scale: float = 1.0                     # E4M3 scales of K and V (R14)
+    v_scale: float = 1.0
     pos: np.ndarray = field(init=False)      # [k] int64, FREE = -1
     K: np.ndarray = field(init=False)        # [k, d] float64 (exact stored values)
     V: np.ndarray = field(init=False)
+    Kc: np.ndarray = field(init=False)       # [k, d] uint8 E4M3 codes ("e4m3" only)
+    Vc: np.ndarray = field(init=False)
     acc: np.ndarray = field(init=False)      # [k] float32 accumulated score
     hist32: dict = field(init=False)         # position -> fp32 score (frozen on eviction)
     hist64: dict = field(init=False)         # position -> float64 shadow score
@@ -178,10 +245,17 @@ class UnitCache:
         if (self.policy == "sinks" and self.policy_param < 0) or \
                 (self.policy == "strided" and self.policy_param < 1):
             raise ValueError(f"bad parameter {self.policy_param} for policy {self.policy!r}")
+        if self.slot_format not in SLOT_FORMATS:
+            raise ValueError(f"unknown slot format {self.slot_format!r}")
+        if self.slot_format == "e4m3" and not all(
+                math.isfinite(x) and x > 0 for x in (self.k_scale, self.v_scale)):
+            raise ValueError("E4M3 scales must be finite and > 0 (R14)")
         k = self.k
         self.pos = np.full(k, FREE, dtype=np.int64)
         self.K = np.zeros((k, self.head_dim))
         self.V = np.zeros((k, self.head_dim))
+        self.Kc = np.zeros((k, self.head_dim), dtype=np.uint8)
+        self.Vc = np.zeros((k, self.head_dim), dtype=np.uint8)
         self.acc = np.zeros(k, dtype=np.float32)
         self.hist32, self.hist64 = {}, {}
         self.evictions, self.ties = [], []
@@ -197,6 +271,19 @@ class UnitCache:
 
     def kept_positions(self) -> list[int]:
         return sorted(int(p) for p in self.pos if p != FREE)
+
+    def stored(self, k_row, v_row):
+        """What a slot holds for these K/V rows: (k value, v value, k codes, v codes)."""
+        if self.slot_format == "e4m3":
+            kc, kv = quantize_row(k_row, self.k_scale)
+            vc, vv = quantize_row(v_row, self.v_scale)
+            return kv, vv, kc, vc
+        return np.asarray(k_row, np.float64), np.asarray(v_row, np.float64), None, None
+
+    def write(self, slot, k_row, v_row):
+        self.K[slot], self.V[slot], kc, vc = self.stored(k_row, v_row)
+        if kc is not None:
+            self.Kc[slot], self.Vc[slot] = kc, vc
 
 
 def _near(a: float, b: float, rel_tol: float) -> bool:
@@ -243,8 +330,7 @@ def prefill(cache: UnitCache, Q, K, V, adopt_kept=None, rel_tol=1e-5):
         cache.hist64[j] = float(c64[j])
     for s, p in enumerate(kept):
         cache.pos[s] = p
-        cache.K[s] = K[p]
-        cache.V[s] = V[p]
+        cache.write(s, K[p], V[p])
         cache.acc[s] = c32[p]
     dropped = sorted(set(range(T)) - set(kept))
     for p in dropped:
@@ -280,6 +366,8 @@ def decode(cache: UnitCache, t: int, q, k_new, v_new, adopt_victim=None,
     slot or -1 when the token was appended.
     """
     q, k_new, v_new = (np.asarray(x, dtype=np.float64) for x in (q, k_new, v_new))
+    k_in, v_in = k_new, v_new
+    k_new, v_new, _, _ = cache.stored(k_in, v_in)    # what the new token's slot will hold (R14)
     n = cache.n_valid
     assert np.all(cache.pos[:n] != FREE) and np.all(cache.pos[n:] == FREE), \
         "valid slots must be a prefix"
@@ -324,8 +412,7 @@ def decode(cache: UnitCache, t: int, q, k_new, v_new, adopt_victim=None,
         cache.evictions.append((t, slot, int(cache.pos[slot]), cache.acc[slot]))
 
     cache.pos[slot] = t
-    cache.K[slot] = k_new
-    cache.V[slot] = v_new
+    cache.write(slot, k_in, v_in)
     cache.acc[slot] = acc_new
     return out, victim
 
@@ -335,13 +422,14 @@ def decode(cache: UnitCache, t: int, q, k_new, v_new, adopt_victim=None,
 # ---------------------------------------------------------------------------
 
 def run_unit(k_heavy, k_local, Qp, Kp, Vp, qd, kd, vd, t0=None,
-             adopt_kept=None, adopt_victims=None, rel_tol=1e-5):
+             adopt_kept=None, adopt_victims=None, rel_tol=1e-5, **cache_kw):
     """Prefill with Qp/Kp/Vp ([T, d]) then decode rows of qd/kd/vd ([n, d]).
 
+    cache_kw are further UnitCache fields (policy, slot format, scales).
     Returns (cache, O_prefill, c64, outs [n, d], victims [n]).
     """
     d = np.asarray(Qp).shape[-1] if np.asarray(Qp).size else np.asarray(qd).shape[-1]
-    cache = UnitCache(k_heavy, k_local, d)
+    cache = UnitCache(k_heavy, k_local, d, **cache_kw)
     O, c64 = prefill(cache, Qp, Kp, Vp, adopt_kept=adopt_kept, rel_tol=rel_tol)
     T = np.asarray(Qp).shape[0] if t0 is None else t0
     n = np.asarray(qd).shape[0]

@@ -409,3 +409,126 @@ def test_policy_parameters_are_checked():
         UnitCache(2, 2, 8, policy="sinks", policy_param=-1)
     with pytest.raises(ValueError):
         UnitCache(2, 2, 8, policy="lru")
+
+
+# ---------------------------------------------------------------------------
+# E4M3 slots ([blog] §3.3 Q3: H2O with KV quantisation; the format is the OCP FP8 E4M3
+# of the oracle's reading R14)
+# ---------------------------------------------------------------------------
+
+from oracle import e4m3_decode, e4m3_encode, e4m3_round, quantize_row  # noqa: E402
+
+
+def _torch_e4m3(x32):
+    """torch's own float32 -> float8_e4m3fn conversion (round to nearest even)."""
+    t = torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32)).to(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy(), t.view(torch.uint8).numpy()
+
+
+def _all_finite(dtype):
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    if dtype == "f16":
+        x = bits.astype(np.uint16).view(np.float16).astype(np.float32)
+    else:
+        x = (bits << 16).view(np.float32)
+    return x[np.isfinite(x)]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_e4m3_matches_the_library_conversion_on_every_half_value(dtype):
+    # Every finite fp16 / bf16 value inside the E4M3 range, plus random fp32 values
+    # spread over all binades, against torch's float8_e4m3fn cast.
+    x = _all_finite(dtype)
+    rng = np.random.default_rng(0)
+    r32 = (rng.choice([-1.0, 1.0], 20000) * np.exp2(rng.uniform(-14, 8.8, 20000))).astype(np.float32)
+    x = np.concatenate([x[np.abs(x) <= 448.0], r32[np.abs(r32) <= 448.0]])
+    want, codes = _torch_e4m3(x)
+    got = e4m3_round(x)
+    assert np.array_equal(got, want)
+    assert np.array_equal(np.signbit(got), np.signbit(want))
+    assert np.array_equal(e4m3_encode(got), codes)
+
+
+def test_e4m3_closed_forms():
+    cases = {  # value -> (rounded value, code), from the E4M3 layout by hand
+        448.0: (448.0, 0x7E), -448.0: (-448.0, 0xFE),
+        1000.0: (448.0, 0x7E), -1e9: (-448.0, 0xFE),           # saturation
+        1.0: (1.0, 0x38), 1.0625: (1.0, 0x38),                 # tie 1 + 1/16 goes to even
+        1.1875: (1.25, 0x3A), 1.125: (1.125, 0x39),            # tie 1 + 3/16 goes up to even
+        2.0 ** -6: (2.0 ** -6, 0x08),                          # smallest normal
+        2.0 ** -9: (2.0 ** -9, 0x01),                          # smallest subnormal
+        2.0 ** -10: (0.0, 0x00), 3 * 2.0 ** -10: (2 * 2.0 ** -9, 0x02),
+        7 * 2.0 ** -9: (7 * 2.0 ** -9, 0x07), 0.0: (0.0, 0x00),
+        240.0: (240.0, 0x77), 232.0: (224.0, 0x76), 248.0: (256.0, 0x78),
+    }
+    for x, (r, code) in cases.items():
+        got = e4m3_round(np.float32(x))
+        assert float(got) == r, x
+        assert int(e4m3_encode(got)) == code, x
+        assert float(e4m3_decode(code)) == r, x
+
+
+def test_e4m3_codes_round_trip():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    vals = e4m3_decode(codes)
+    assert np.array_equal(e4m3_round(vals), vals)
+    assert np.array_equal(e4m3_encode(vals), codes)
+    assert np.isnan(e4m3_decode(np.array([0x7F, 0xFF]))).all()
+    assert float(np.nanmax(np.abs(vals))) == 448.0
+
+
+def test_quantize_row_scale_by_hand():
+    # scale 3: 1/3 in fp32 is 0x3EAAAAAB = 0.3333333432674408; 1.0 times it is the same;
+    # E4M3 steps of 2^-5 in [0.25, 0.5): 0.33333 / 0.03125 = 10.67 -> 11 -> 0.34375,
+    # code 0 0101 011 = 0x2B; read back 0.34375 * 3 = 1.03125.
+    codes, vals = quantize_row(np.array([1.0, -1.0, 0.0, 2000.0]), 3.0)
+    assert list(codes) == [0x2B, 0xAB, 0x00, 0x7E]
+    assert list(vals) == [1.03125, -1.03125, 0.0, 448.0 * 3]
+
+
+def _e4m3_exact(rng, shape, scale):
+    """Values that E4M3 holds exactly, times scale: integers in [-15, 15] / 4."""
+    return rng.integers(-15, 16, size=shape) / 4.0 * scale
+
+
+@pytest.mark.parametrize("scale", [1.0, 2.0, 0.125])
+def test_e4m3_slots_reduce_to_plain_slots_on_representable_rows(scale):
+    # When every K/V row is a representable value times a power-of-two scale, quantising
+    # changes nothing: the E4M3 cache must then match the unquantised one step for step.
+    rng = np.random.default_rng(3)
+    T, n, d, kh, kl = 20, 15, 8, 3, 4
+    Q = rng.standard_normal((T + n, d))
+    K, V = _e4m3_exact(rng, (T + n, d), scale), _e4m3_exact(rng, (T + n, d), scale)
+    a = run_unit(kh, kl, Q[:T], K[:T], V[:T], Q[T:], K[T:], V[T:])
+    b = run_unit(kh, kl, Q[:T], K[:T], V[:T], Q[T:], K[T:], V[T:],
+                 slot_format="e4m3", k_scale=scale, v_scale=scale)
+    assert np.array_equal(a[3], b[3]) and np.array_equal(a[4], b[4])
+    assert np.array_equal(a[0].K, b[0].K) and np.array_equal(a[0].pos, b[0].pos)
+
+
+def test_e4m3_step_attends_to_what_the_cache_then_holds():
+    # While the cache fills nothing leaves, so after each step the valid slots are exactly
+    # the keys the step attended to: its output must be attention over the stored rows,
+    # and the stored codes must decode to the stored values.
+    rng = np.random.default_rng(4)
+    d = 16
+    cache = UnitCache(6, 4, d, slot_format="e4m3", k_scale=0.37, v_scale=1.9)
+    for t in range(9):
+        q, k, v = (rng.standard_normal(d) * 3 for _ in range(3))
+        out, victim = decode(cache, t, q, k, v)
+        assert victim == -1
+        n = t + 1
+        s = cache.K[:n] @ q / math.sqrt(d)
+        p = np.exp(s - s.max())
+        np.testing.assert_allclose(out, (p / p.sum()) @ cache.V[:n], rtol=1e-12, atol=1e-12)
+        assert np.array_equal(e4m3_decode(cache.Kc[:n]) * float(np.float32(0.37)), cache.K[:n])
+        assert np.array_equal(e4m3_decode(cache.Vc[:n]) * float(np.float32(1.9)), cache.V[:n])
+
+
+def test_e4m3_slot_parameters_are_checked():
+    with pytest.raises(ValueError):
+        UnitCache(2, 2, 8, slot_format="e5m2")
+    with pytest.raises(ValueError):
+        UnitCache(2, 2, 8, slot_format="e4m3", k_scale=0.0)
+    with pytest.raises(ValueError):
+        UnitCache(2, 2, 8, slot_format="e4m3", v_scale=float("inf"))
