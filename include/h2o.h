@@ -35,7 +35,8 @@
  * interface. Misuse that cannot be checked (decode positions out of order,
  * buffers that are too small) is undefined behaviour.
  *
- * Numerics. Q/K/V and the K/V slots are stored in `dtype`; all arithmetic is
+ * Numerics. Q/K/V are stored in `dtype`, the K/V slots in `dtype` or, on
+ * request, as FP8 E4M3 codes (h2o_slot_format below); all arithmetic is
  * fp32. Attention outputs are written as fp32. Scores (acc_score) are fp32:
  * prefill seeds a slot with its fp32 column sum, each decode step adds the
  * token's fp32 probability with one fp32 add. Eviction decisions are taken on
@@ -89,6 +90,25 @@ typedef enum {
   H2O_POLICY_TOPK = 3
 } h2o_policy;
 
+/*
+ * Slot storage. The H2O blog (§3.3 Q3) reports that H2O combines with KV
+ * quantisation and names no scheme; this build offers OCP FP8 E4M3 slots:
+ *   H2O_SLOTS_INPUT     k_slots / v_slots hold K/V in dtype (the default)
+ *   H2O_SLOTS_FP8_E4M3  they hold E4M3 codes, one byte per element (1 sign,
+ *                       4 exponent bits with bias 7, 3 mantissa bits; largest
+ *                       finite value 448). A K row x enters a slot as codes
+ *                       e4m3(fl32(x * fl32(1 / k_scale))), rounded to nearest
+ *                       with ties to even and saturated at +-448, and is read
+ *                       back as code value * k_scale (V likewise with v_scale).
+ *                       The new token's K/V are quantised before the step's
+ *                       attention reads them, so a step attends to exactly
+ *                       what the cache holds afterwards; prefill attention
+ *                       reads the prompt's own K/V. dtype must be H2O_F16 or
+ *                       H2O_BF16 (H2O_ERR_UNSUPPORTED for H2O_F32); k_scale
+ *                       and v_scale must be finite and > 0.
+ */
+typedef enum { H2O_SLOTS_INPUT = 0, H2O_SLOTS_FP8_E4M3 = 1 } h2o_slot_format;
+
 /* Limits of this build. */
 #define H2O_MAX_SLOTS 8192        /* k = k_heavy + k_local */
 #define H2O_MAX_POSITION 0x7fffffff
@@ -101,11 +121,15 @@ typedef enum {
  *   k_heavy       >= 0 ; k_local >= 1 ; 1 <= k_heavy + k_local <= H2O_MAX_SLOTS
  *                 (k_local >= 1 keeps the new token out of the candidates:
  *                 the recent window is positions (t - k_local, t])
- *   dtype         storage type of Q/K/V and of k_slots/v_slots (h2o_dtype)
- *   k_slots, v_slots  16-byte aligned
+ *   dtype         storage type of Q/K/V, and of k_slots/v_slots unless
+ *                 slot_format says otherwise (h2o_dtype)
+ *   k_slots, v_slots  16-byte aligned; [batch][heads][k][head_dim] elements of
+ *                 dtype, or of one byte with H2O_SLOTS_FP8_E4M3
  *   slot_pos      int32 absolute position held by each slot, -1 = free
  *   acc_score     fp32 accumulated attention score of each slot
  *   policy, policy_param  eviction ranking (h2o_policy above); 0, 0 is H2O
+ *   slot_format   h2o_slot_format; 0 stores the slots in dtype
+ *   k_scale, v_scale  E4M3 scales (read only with H2O_SLOTS_FP8_E4M3)
  * Valid slots always form a prefix [0, n_valid) of each unit's slots.
  */
 typedef struct {
@@ -121,6 +145,9 @@ typedef struct {
   float* acc_score;
   int32_t policy;
   int32_t policy_param;
+  int32_t slot_format;
+  float k_scale;
+  float v_scale;
 } h2o_cache_desc;
 
 /*

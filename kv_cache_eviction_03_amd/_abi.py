@@ -9,7 +9,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from ctypes import c_char_p, c_int32, c_int64, c_size_t, c_void_p
+from ctypes import c_char_p, c_float, c_int32, c_int64, c_size_t, c_void_p
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libh2o.so")
 
@@ -18,6 +18,8 @@ H2O_F32, H2O_F16, H2O_BF16 = range(3)
 H2O_POLICY_H2O, H2O_POLICY_SINKS, H2O_POLICY_STRIDED, H2O_POLICY_TOPK = range(4)
 POLICY_CODES = {"h2o": H2O_POLICY_H2O, "sinks": H2O_POLICY_SINKS,
                 "strided": H2O_POLICY_STRIDED, "topk": H2O_POLICY_TOPK}
+H2O_SLOTS_INPUT, H2O_SLOTS_FP8_E4M3 = range(2)
+SLOT_FORMAT_CODES = {"input": H2O_SLOTS_INPUT, "e4m3": H2O_SLOTS_FP8_E4M3}
 H2O_MAX_SLOTS = 8192
 
 EXPORTS = ("h2o_reset", "h2o_workspace_bytes", "h2o_prefill", "h2o_decode_step",
@@ -30,7 +32,8 @@ class CacheDesc(ctypes.Structure):
                 ("k_heavy", c_int32), ("k_local", c_int32), ("dtype", c_int32),
                 ("k_slots", c_void_p), ("v_slots", c_void_p),
                 ("slot_pos", c_void_p), ("acc_score", c_void_p),
-                ("policy", c_int32), ("policy_param", c_int32)]
+                ("policy", c_int32), ("policy_param", c_int32),
+                ("slot_format", c_int32), ("k_scale", c_float), ("v_scale", c_float)]
 
 
 class DecodeAux(ctypes.Structure):

@@ -8,7 +8,8 @@ from __future__ import annotations
 
 import torch
 
-from ._abi import (H2O_BF16, H2O_F16, H2O_F32, POLICY_CODES, CacheDesc, DecodeAux, check,
+from ._abi import (H2O_BF16, H2O_F16, H2O_F32, POLICY_CODES, SLOT_FORMAT_CODES, CacheDesc,
+                   DecodeAux, check,
                    h2o_decode_step,
                    h2o_decode_step_ragged, h2o_prefill, h2o_prefill_ragged, h2o_reset,
                    h2o_workspace_bytes)
@@ -26,16 +27,22 @@ def _ptr(x: torch.Tensor | None) -> int:
 
 class H2OCache:
     """k = k_heavy + k_local slots per (sequence, head) of one layer; `policy` picks the
-    eviction ranking (h2o, sinks, strided, topk; see include/h2o.h)."""
+    eviction ranking (h2o, sinks, strided, topk), `slot_format` the slot storage ("input":
+    the input dtype; "e4m3": FP8 E4M3 codes with scales k_scale / v_scale, held as
+    torch.float8_e4m3fn tensors). See include/h2o.h."""
 
     def __init__(self, batch: int, heads: int, head_dim: int, k_heavy: int, k_local: int,
                  dtype: torch.dtype, device="cuda", max_prompt: int = 0, policy: str = "h2o",
-                 policy_param: int = 0):
+                 policy_param: int = 0, slot_format: str = "input", k_scale: float = 1.0,
+                 v_scale: float = 1.0):
         if dtype not in _DTYPE_CODE:
             raise ValueError(f"unsupported dtype {dtype}")
         if policy not in POLICY_CODES:
             raise ValueError(f"unknown policy {policy!r}")
+        if slot_format not in SLOT_FORMAT_CODES:
+            raise ValueError(f"unknown slot format {slot_format!r}")
         self.policy, self.policy_param = policy, policy_param
+        self.slot_format, self.k_scale, self.v_scale = slot_format, k_scale, v_scale
         self.batch, self.heads, self.head_dim = batch, heads, head_dim
         self.k_heavy, self.k_local = k_heavy, k_local
         self.k = k_heavy + k_local
@@ -45,8 +52,9 @@ class H2OCache:
             dev = torch.device("cuda", torch.cuda.current_device())
         self.device = dev
         shape = (batch, heads, self.k, head_dim)
-        self.k_slots = torch.zeros(shape, dtype=dtype, device=self.device)
-        self.v_slots = torch.zeros(shape, dtype=dtype, device=self.device)
+        sdt = torch.float8_e4m3fn if slot_format == "e4m3" else dtype
+        self.k_slots = torch.zeros(shape, dtype=sdt, device=self.device)
+        self.v_slots = torch.zeros(shape, dtype=sdt, device=self.device)
         self.slot_pos = torch.full((batch, heads, self.k), -1, dtype=torch.int32,
                                    device=self.device)
         self.acc_score = torch.zeros((batch, heads, self.k), dtype=torch.float32,
@@ -60,7 +68,8 @@ class H2OCache:
                          _DTYPE_CODE[self.dtype], self.k_slots.data_ptr(),
                          self.v_slots.data_ptr(), self.slot_pos.data_ptr(),
                          self.acc_score.data_ptr(), POLICY_CODES[self.policy],
-                         self.policy_param)
+                         self.policy_param, SLOT_FORMAT_CODES[self.slot_format], self.k_scale,
+                         self.v_scale)
 
     def reserve(self, max_prompt: int) -> None:
         need = h2o_workspace_bytes(self.desc(), max_prompt)

@@ -65,19 +65,43 @@ __device__ __forceinline__ float row_sum(float v) {
   return v;
 }
 
-// Loads of one row group: K and V chunks of its U slots (clamped to the new token row).
-template <typename T, int D, int U, int THREADS>
-__device__ __forceinline__ void load_rows(const T* ks, const T* vs, const T* kn, const T* vn,
-                                          int first, int n, int rl, uint4 (&kr)[U],
-                                          uint4 (&vr)[U]) {
+// Loads of one row group: K and V chunks of its U slots. Rows past the valid slots are
+// clamped to the new token's row (slots stored in T) or to slot 0 (E4M3 slots, whose rows
+// are replaced by the new token's codes once those are formed: fill_new_rows).
+template <typename T, int D, int U, int THREADS, bool F8>
+__device__ __forceinline__ void load_rows(const typename SlotChunk<T, F8>::elem* ks,
+                                          const typename SlotChunk<T, F8>::elem* vs,
+                                          const T* kn, const T* vn, int first, int n, int rl,
+                                          typename SlotChunk<T, F8>::type (&kr)[U],
+                                          typename SlotChunk<T, F8>::type (&vr)[U]) {
   using S = Shape<T, D, THREADS>;
+  using SC = SlotChunk<T, F8>;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int j = first + u * S::ROWS;
     const bool slot = j < n;
     const size_t off = (size_t)(slot ? j : 0) * D + rl * S::VEC;
-    kr[u] = ld16(slot ? ks + off : kn + rl * S::VEC);
-    vr[u] = ld16(slot ? vs + off : vn + rl * S::VEC);
+    if constexpr (F8) {
+      kr[u] = SC::load(ks + off);
+      vr[u] = SC::load(vs + off);
+    } else {
+      kr[u] = ld16(slot ? ks + off : kn + rl * S::VEC);
+      vr[u] = ld16(slot ? vs + off : vn + rl * S::VEC);
+    }
+  }
+}
+
+// E4M3 slots: the new token's K/V join as codes before attention reads them, so rows at
+// and past the valid slots take the new token's codes.
+template <typename T, int D, int U, int THREADS>
+__device__ __forceinline__ void fill_new_rows(int first, int n, const uint2& knq, const uint2& vnq,
+                                              uint2 (&kr)[U], uint2 (&vr)[U]) {
+  using S = Shape<T, D, THREADS>;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const bool slot = first + u * S::ROWS < n;
+    kr[u] = slot ? kr[u] : knq;
+    vr[u] = slot ? vr[u] : vnq;
   }
 }
 
@@ -106,12 +130,34 @@ __device__ __forceinline__ float chunk_dot(const uint4& a, const uint4& b, float
                                         c, false);
   return c;
 }
+// q chunk (8 elements of T) against 8 E4M3 codes: each code pair is widened to a T pair
+// (exact: E4M3 values are fp16 and bf16 values) and fed to v_dot2.
+__device__ __forceinline__ float chunk_dot(const uint4& a, const uint2& b, float c, _Float16) {
+  const f16x2 k0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)b.x, 1.0f, false);
+  const f16x2 k1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)b.x, 1.0f, true);
+  const f16x2 k2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)b.y, 1.0f, false);
+  const f16x2 k3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)b.y, 1.0f, true);
+  c = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a.x), k0, c, false);
+  c = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a.y), k1, c, false);
+  c = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a.z), k2, c, false);
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a.w), k3, c, false);
+}
+__device__ __forceinline__ float chunk_dot(const uint4& a, const uint2& b, float c, __bf16) {
+  const bf16x2 k0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)b.x, 1.0f, false);
+  const bf16x2 k1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)b.x, 1.0f, true);
+  const bf16x2 k2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)b.y, 1.0f, false);
+  const bf16x2 k3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)b.y, 1.0f, true);
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.x), k0, c, false);
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.y), k1, c, false);
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.z), k2, c, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.w), k3, c, false);
+}
 
 // Logits (log2 domain) of a row group's U slots; slots past `last` are -inf.
 // Returns the group max, its sum of 2^(s - max) and the unnormalised out chunk.
-template <typename T, int D, int U, int THREADS>
-__device__ __forceinline__ void group_softmax(const uint4& qr, float qk_scale, const uint4 (&kr)[U],
-                                              const uint4 (&vr)[U], int first, int last,
+template <typename T, int D, int U, int THREADS, typename C>
+__device__ __forceinline__ void group_softmax(const uint4& qr, float qk_scale, const C (&kr)[U],
+                                              const C (&vr)[U], int first, int last,
                                               float (&s)[U], float& mg, float& lg,
                                               float (&o)[Shape<T, D>::VEC]) {
   using S = Shape<T, D, THREADS>;
@@ -145,13 +191,15 @@ __device__ __forceinline__ uint64_t score_key(float a, int pos) {
 
 // ------------------------------------------------------------------ resident --
 
-template <typename T, int D, int THREADS>
+template <typename T, int D, int THREADS, bool F8>
 // Register budget: at most 128 VGPRs for the 256-thread shape, so that at least four
 // workgroups share a CU (three per CU measured 3.5% slower on the 32-layer LLaMA-7B-shaped
 // stack). The kernels currently need about 92.
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS == 256 ? 4 : 1, 8)))
 void decode_resident_kernel(DecodeParams p) {
   using S = Shape<T, D, THREADS>;
+  using SC = SlotChunk<T, F8>;
+  using SE = typename SC::elem;
   constexpr int VEC = S::VEC, LANES = S::LANES, ROWS = S::ROWS, U = kBatch;
   static_assert(U <= LANES, "a lane owns one slot score");
   __shared__ __attribute__((aligned(16))) float s_red[ROWS * D];
@@ -168,8 +216,8 @@ void decode_resident_kernel(DecodeParams p) {
   const bool full = n == k;
   const int limit = t - p.k_local;
 
-  T* ks = static_cast<T*>(p.k_slots) + (size_t)unit * k * D;
-  T* vs = static_cast<T*>(p.v_slots) + (size_t)unit * k * D;
+  SE* ks = static_cast<SE*>(p.k_slots) + (size_t)unit * k * D;
+  SE* vs = static_cast<SE*>(p.v_slots) + (size_t)unit * k * D;
   const T* kn = static_cast<const T*>(p.k_new) + (size_t)unit * D;
   const T* vn = static_cast<const T*>(p.v_new) + (size_t)unit * D;
   int32_t* pos = p.slot_pos + (size_t)unit * k;
@@ -177,8 +225,8 @@ void decode_resident_kernel(DecodeParams p) {
 
   // Every load of the unit, issued before any is consumed.
   const uint4 qr = ld16(static_cast<const T*>(p.q) + (size_t)unit * D + rl * VEC);
-  uint4 kr[U], vr[U];
-  load_rows<T, D, U, THREADS>(ks, vs, kn, vn, g, n, rl, kr, vr);
+  typename SC::type kr[U], vr[U];
+  load_rows<T, D, U, THREADS, F8>(ks, vs, kn, vn, g, n, rl, kr, vr);
   const int jo = rl * ROWS + g;                 // slot whose score this lane owns
   const bool own = rl < U && jo < n;
   const int jc = own ? jo : 0;
@@ -187,6 +235,16 @@ void decode_resident_kernel(DecodeParams p) {
   const uint4 knr = ld16(kn + rl * VEC), vnr = ld16(vn + rl * VEC);
   __builtin_amdgcn_sched_barrier(0);            // keep every load ahead of the math
 
+  // The new token's row as it will be stored.
+  typename SC::type kst, vst;
+  if constexpr (F8) {
+    kst = quant_e4m3<T>(knr, p.k_inv);
+    vst = quant_e4m3<T>(vnr, p.v_inv);
+    fill_new_rows<T, D, U, THREADS>(g, n, kst, vst, kr, vr);
+  } else {
+    kst = knr;
+    vst = vnr;
+  }
   float s[U], mg, lg, o[VEC];
   group_softmax<T, D, U, THREADS>(qr, p.qk_scale, kr, vr, g, n, s, mg, lg, o);
 
@@ -216,6 +274,7 @@ void decode_resident_kernel(DecodeParams p) {
   const float l_ab = (in_a ? l_a0 * sc_a : 0.f) + (in_b ? l_b0 * sc_b : 0.f);
   const float inv = __builtin_amdgcn_rcpf(wave_sum_uniform(l_ab));
   const float p_new = fast_exp2(lg_new - M) * inv;
+  const float out_scale = F8 ? inv * p.v_scale : inv;   // E4M3: values in code units until here
   if (lane < ROWS) s_scw[wave][lane] = sc_a;
   if (lane + kWave < ROWS) s_scw[wave][lane + kWave] = sc_b;
 
@@ -233,7 +292,7 @@ void decode_resident_kernel(DecodeParams p) {
     }
 #pragma unroll
     for (int w = CW; w < kWave; w *= 2) v += __shfl_xor(v, w, kWave);
-    if (sl == 0) p.out[(size_t)unit * D + c] = v * inv;
+    if (sl == 0) p.out[(size_t)unit * D + c] = v * out_scale;
   }
 
   uint64_t key = ~0ull;
@@ -264,8 +323,8 @@ void decode_resident_kernel(DecodeParams p) {
     meta = jo == n;
   }
   if (dst >= 0) {
-    st16(ks + (size_t)dst * D + rl * VEC, knr);
-    st16(vs + (size_t)dst * D + rl * VEC, vnr);
+    SC::store(ks + (size_t)dst * D + rl * VEC, kst);
+    SC::store(vs + (size_t)dst * D + rl * VEC, vst);
   }
   if (meta) {                                   // the lane that wrote acc[dst] above, if any
     pos[dst] = t;
@@ -281,10 +340,12 @@ void decode_resident_kernel(DecodeParams p) {
 constexpr int kPartThreads = 256;
 constexpr int kCombThreads = 1024;
 
-template <typename T, int D>
+template <typename T, int D, bool F8>
 __global__ __launch_bounds__(kPartThreads) void decode_split_partial_kernel(DecodeParams p,
                                                                             SplitScratch w) {
   using S = Shape<T, D, kPartThreads>;
+  using SC = SlotChunk<T, F8>;
+  using SE = typename SC::elem;
   constexpr int VEC = S::VEC, LANES = S::LANES, ROWS = S::ROWS, U = kBatch;
   constexpr int C = ROWS * U;                   // slots per workgroup
   __shared__ __attribute__((aligned(16))) float s_red[ROWS * D];
@@ -295,8 +356,8 @@ __global__ __launch_bounds__(kPartThreads) void decode_split_partial_kernel(Deco
   const int tid = threadIdx.x;
   const int rl = tid % LANES, g = tid / LANES;
   const int k = p.k, n = min(k, unit_bound(p.tpos, unit, p.heads, p.t, 0x7ffffffe));
-  const T* ks = static_cast<const T*>(p.k_slots) + (size_t)unit * k * D;
-  const T* vs = static_cast<const T*>(p.v_slots) + (size_t)unit * k * D;
+  const SE* ks = static_cast<const SE*>(p.k_slots) + (size_t)unit * k * D;
+  const SE* vs = static_cast<const SE*>(p.v_slots) + (size_t)unit * k * D;
   const T* kn = static_cast<const T*>(p.k_new) + (size_t)unit * D;
   const T* vn = static_cast<const T*>(p.v_new) + (size_t)unit * D;
   float* logit = w.logits + (size_t)unit * (k + 1);
@@ -304,9 +365,17 @@ __global__ __launch_bounds__(kPartThreads) void decode_split_partial_kernel(Deco
   // This workgroup's chunk [sp*C, sp*C + C) of the n + 1 keys.
   const int first = sp * C + g;
   const uint4 qr = ld16(static_cast<const T*>(p.q) + (size_t)unit * D + rl * VEC);
-  uint4 kr[U], vr[U];
-  load_rows<T, D, U, kPartThreads>(ks, vs, kn, vn, first, n, rl, kr, vr);
+  typename SC::type kr[U], vr[U];
+  load_rows<T, D, U, kPartThreads, F8>(ks, vs, kn, vn, first, n, rl, kr, vr);
+  uint4 knr, vnr;
+  if constexpr (F8) {
+    knr = ld16(kn + rl * VEC);
+    vnr = ld16(vn + rl * VEC);
+  }
   __builtin_amdgcn_sched_barrier(0);            // keep every load ahead of the math
+  if constexpr (F8)
+    fill_new_rows<T, D, U, kPartThreads>(first, n, quant_e4m3<T>(knr, p.k_inv),
+                                         quant_e4m3<T>(vnr, p.v_inv), kr, vr);
   float s[U], mg, lg, o[VEC];
   group_softmax<T, D, U, kPartThreads>(qr, p.qk_scale, kr, vr, first, n, s, mg, lg, o);
   if (rl == 0) {
@@ -353,9 +422,11 @@ __global__ __launch_bounds__(kPartThreads) void decode_split_partial_kernel(Deco
 // scores and positions; the new token's logit and K/V) is issued before any is
 // consumed. Further batches (more than QB * G splits or R * kCombThreads slots) follow
 // in loops.
-template <typename T, int D>
+template <typename T, int D, bool F8>
 __global__ __launch_bounds__(kCombThreads) void decode_split_combine_kernel(DecodeParams p,
                                                                             SplitScratch w) {
+  using SC = SlotChunk<T, F8>;
+  using SE = typename SC::elem;
   constexpr int VEC = Chunk<T>::N, LANES = D / VEC;
   constexpr int WAVES = kCombThreads / kWave;
   constexpr int G = kCombThreads / D;           // groups that share the partial-out sums
@@ -374,8 +445,8 @@ __global__ __launch_bounds__(kCombThreads) void decode_split_combine_kernel(Deco
   const int n = min(k, t);
   const bool full = n == k;
   const int limit = t - p.k_local;
-  T* ks = static_cast<T*>(p.k_slots) + (size_t)unit * k * D;
-  T* vs = static_cast<T*>(p.v_slots) + (size_t)unit * k * D;
+  SE* ks = static_cast<SE*>(p.k_slots) + (size_t)unit * k * D;
+  SE* vs = static_cast<SE*>(p.v_slots) + (size_t)unit * k * D;
   const T* kn = static_cast<const T*>(p.k_new) + (size_t)unit * D;
   const T* vn = static_cast<const T*>(p.v_new) + (size_t)unit * D;
   int32_t* pos = p.slot_pos + (size_t)unit * k;
@@ -427,6 +498,7 @@ __global__ __launch_bounds__(kCombThreads) void decode_split_combine_kernel(Deco
     l = fmaf(pl[i], sc, l);
   }
   const float inv = 1.0f / wave_sum_uniform(l);
+  const float out_scale = F8 ? inv * p.v_scale : inv;   // E4M3: values in code units until here
 
   // out: G groups of D threads each sum every G-th partial, then a fixed-order merge.
   {
@@ -472,7 +544,7 @@ __global__ __launch_bounds__(kCombThreads) void decode_split_combine_kernel(Deco
     float v = 0.f;
 #pragma unroll
     for (int gi = 0; gi < G; ++gi) v += s_o[gi * D + tid];
-    p.out[(size_t)unit * D + tid] = v * inv;
+    p.out[(size_t)unit * D + tid] = v * out_scale;
   }
   uint64_t gbest = s_key[0];
 #pragma unroll
@@ -483,7 +555,13 @@ __global__ __launch_bounds__(kCombThreads) void decode_split_combine_kernel(Deco
   __syncthreads();
   const int dst = s_dst;
   if (dst >= 0) {
-    if (tid < 2 * LANES) st16((tid < LANES ? ks : vs) + (size_t)dst * D + (tid % LANES) * VEC, kvn);
+    if (tid < 2 * LANES) {
+      SE* row = (tid < LANES ? ks : vs) + (size_t)dst * D + (tid % LANES) * VEC;
+      if constexpr (F8)
+        SC::store(row, quant_e4m3<T>(kvn, tid < LANES ? p.k_inv : p.v_inv));
+      else
+        SC::store(row, kvn);
+    }
     if (tid == dst % kCombThreads) {            // visited slot dst in the score loop
       pos[dst] = t;
       acc[dst] = fast_exp2(lg_new - M) * inv;
@@ -499,20 +577,20 @@ __global__ __launch_bounds__(kCombThreads) void decode_split_combine_kernel(Deco
 
 // ------------------------------------------------------------------ dispatch --
 
-template <typename T, int D>
+template <typename T, int D, bool F8 = false>
 hipError_t run(const DecodeParams& p, const SplitScratch& w, hipStream_t s) {
   const DecodePlan plan = plan_decode(sizeof(T), D, p.k, p.units);
   if (plan.splits == 0) {
     if (plan.threads == 256)
-      decode_resident_kernel<T, D, 256><<<dim3(p.units), dim3(256), 0, s>>>(p);
+      decode_resident_kernel<T, D, 256, F8><<<dim3(p.units), dim3(256), 0, s>>>(p);
     else
-      decode_resident_kernel<T, D, 1024><<<dim3(p.units), dim3(1024), 0, s>>>(p);
+      decode_resident_kernel<T, D, 1024, F8><<<dim3(p.units), dim3(1024), 0, s>>>(p);
     return hipGetLastError();
   }
-  decode_split_partial_kernel<T, D>
+  decode_split_partial_kernel<T, D, F8>
       <<<dim3((unsigned)(p.units * plan.splits)), dim3(kPartThreads), 0, s>>>(p, w);
   if (hipError_t e = hipGetLastError()) return e;
-  decode_split_combine_kernel<T, D><<<dim3(p.units), dim3(kCombThreads), 0, s>>>(p, w);
+  decode_split_combine_kernel<T, D, F8><<<dim3(p.units), dim3(kCombThreads), 0, s>>>(p, w);
   return hipGetLastError();
 }
 
@@ -551,8 +629,12 @@ SplitScratch carve_decode_scratch(int elem_bytes, int D, int k, int units, void*
   return w;
 }
 
-hipError_t launch_decode(DType dt, int D, const DecodeParams& p, const SplitScratch& w,
+hipError_t launch_decode(DType dt, bool f8, int D, const DecodeParams& p, const SplitScratch& w,
                          hipStream_t s) {
+  if (f8) {
+    if (dt == DType::F16) return D == 64 ? run<_Float16, 64, true>(p, w, s) : run<_Float16, 128, true>(p, w, s);
+    return D == 64 ? run<__bf16, 64, true>(p, w, s) : run<__bf16, 128, true>(p, w, s);
+  }
   switch (dt) {
     case DType::F32: return D == 64 ? run<float, 64>(p, w, s) : run<float, 128>(p, w, s);
     case DType::F16: return D == 64 ? run<_Float16, 64>(p, w, s) : run<_Float16, 128>(p, w, s);

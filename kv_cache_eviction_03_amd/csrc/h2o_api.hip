@@ -56,6 +56,16 @@ h2o_status check_desc(const h2o_cache_desc* c) {
       (c->policy == H2O_POLICY_STRIDED && c->policy_param < 1))
     return fail(H2O_ERR_INVALID, "policy_param %d out of range for policy %d", c->policy_param,
                 c->policy);
+  if (c->slot_format != H2O_SLOTS_INPUT && c->slot_format != H2O_SLOTS_FP8_E4M3)
+    return fail(H2O_ERR_INVALID, "slot_format %d is not an h2o_slot_format", c->slot_format);
+  if (c->slot_format == H2O_SLOTS_FP8_E4M3) {
+    if (c->dtype == H2O_F32)
+      return fail(H2O_ERR_UNSUPPORTED, "E4M3 slots take fp16 or bf16 inputs, not fp32");
+    if (!(std::isfinite(c->k_scale) && c->k_scale > 0.f && std::isfinite(c->v_scale) &&
+          c->v_scale > 0.f))
+      return fail(H2O_ERR_INVALID, "E4M3 scales must be finite and > 0 (k_scale %g, v_scale %g)",
+                  (double)c->k_scale, (double)c->v_scale);
+  }
   if ((int64_t)c->k_heavy + c->k_local > H2O_MAX_SLOTS)
     return fail(H2O_ERR_UNSUPPORTED, "k = %lld exceeds H2O_MAX_SLOTS (%d)",
                 (long long)c->k_heavy + c->k_local, H2O_MAX_SLOTS);
@@ -102,6 +112,9 @@ size_t decode_scratch(const h2o_cache_desc* c) {
 }
 
 h2o::DType dtype_of(const h2o_cache_desc* c) { return static_cast<h2o::DType>(c->dtype); }
+bool f8_of(const h2o_cache_desc* c) { return c->slot_format == H2O_SLOTS_FP8_E4M3; }
+// fl32(1 / scale) of an E4M3 slot format (unused otherwise).
+float inv_of(const h2o_cache_desc* c, float scale) { return f8_of(c) ? 1.0f / scale : 1.0f; }
 
 float qk_scale(int d) { return (float)(1.4426950408889634 / std::sqrt((double)d)); }
 
@@ -190,8 +203,9 @@ h2o_status prefill_impl(const h2o_cache_desc* c, const void* q, const void* k, c
   }
   h2o::SeedParams sp{k, v, colpart, colsum, lens, c->k_slots, c->v_slots, c->slot_pos,
                      c->acc_score, (int32_t)units, c->heads, T, part_rows_of(c, T), c->k_heavy,
-                     c->k_local, c->policy, c->policy_param};
-  if ((e = h2o::launch_seed(dt, D, sp, s))) return hip_fail(e, "seed launch");
+                     c->k_local, c->policy, c->policy_param, inv_of(c, c->k_scale),
+                     inv_of(c, c->v_scale)};
+  if ((e = h2o::launch_seed(dt, f8_of(c), D, sp, s))) return hip_fail(e, "seed launch");
   return H2O_OK;
 }
 
@@ -234,8 +248,11 @@ h2o_status decode_impl(const h2o_cache_desc* c, int64_t t, const int32_t* tpos, 
                       aux ? aux->victim_slot : nullptr, aux ? aux->evicted_pos : nullptr,
                       aux ? aux->evicted_acc : nullptr, tpos, c->policy, c->policy_param,
                       (int32_t)(c->batch * c->heads),
-                      c->heads, kk, c->k_local, (int32_t)t, qk_scale(D)};
-  if (hipError_t e = h2o::launch_decode(dtype_of(c), D, p, w, static_cast<hipStream_t>(stream)))
+                      c->heads, kk, c->k_local, (int32_t)t,
+                      f8_of(c) ? qk_scale(D) * c->k_scale : qk_scale(D), inv_of(c, c->k_scale),
+                      inv_of(c, c->v_scale), f8_of(c) ? c->v_scale : 1.0f};
+  if (hipError_t e = h2o::launch_decode(dtype_of(c), f8_of(c), D, p, w,
+                                        static_cast<hipStream_t>(stream)))
     return hip_fail(e, "decode launch");
   return H2O_OK;
 }

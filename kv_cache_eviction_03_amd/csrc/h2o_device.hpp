@@ -144,6 +144,63 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// ---- OCP FP8 E4M3 slot codes (one byte per element: sign, 4 exponent bits with bias 7,
+// 3 mantissa bits; largest finite value 448). gfx950's conversions use this format.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint2 ld8(const void* p) { return *reinterpret_cast<const uint2*>(p); }
+__device__ __forceinline__ void st8(void* p, const uint2& v) { *reinterpret_cast<uint2*>(p) = v; }
+
+// One 16-byte chunk of T (8 elements) -> its 8 codes: each element times `inv` (one fp32
+// rounding), clamped to +-448, then the hardware's round-to-nearest-even conversion.
+// Element i goes to byte i.
+template <typename T>
+__device__ __forceinline__ uint2 quant_e4m3(const uint4& x, float inv) {
+  float f[8];
+  unpack(x, f, T{});
+  uint32_t w[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    float y[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = __builtin_amdgcn_fmed3f(f[4 * i + e] * inv, -448.f, 448.f);
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], r, true);
+    w[i] = (uint32_t)r;
+  }
+  return make_uint2(w[0], w[1]);
+}
+
+// 8 codes -> fp32 (exact: every E4M3 value is an fp32 value).
+template <typename T>
+__device__ __forceinline__ void unpack(const uint2& v, float (&f)[8], T) {
+  const uint32_t w[2] = {v.x, v.y};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], false);
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[i], true);
+    f[4 * i] = lo.x; f[4 * i + 1] = lo.y; f[4 * i + 2] = hi.x; f[4 * i + 3] = hi.y;
+  }
+}
+
+// Slot storage: a lane's share of a slot row is one 16-byte chunk of T, or, with E4M3
+// slots (F8), the 8 codes of the same elements.
+template <typename T, bool F8> struct SlotChunk {
+  typedef uint4 type;
+  typedef T elem;
+  __device__ static type load(const elem* p) { return ld16(p); }
+  __device__ static void store(elem* p, const type& v) { st16(p, v); }
+};
+template <typename T> struct SlotChunk<T, true> {
+  static_assert(sizeof(T) == 2, "E4M3 slots take fp16 or bf16 inputs");
+  typedef uint2 type;
+  typedef uint8_t elem;
+  __device__ static type load(const elem* p) { return ld8(p); }
+  __device__ static void store(elem* p, const type& v) { st8(p, v); }
+};
+
 template <typename T> struct Vec8;
 template <> struct Vec8<_Float16> { typedef f16x8 type; typedef f16x4 half; };
 template <> struct Vec8<__bf16> { typedef bf16x8 type; typedef bf16x4 half; };

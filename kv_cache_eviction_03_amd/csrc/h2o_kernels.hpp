@@ -60,7 +60,9 @@ struct DecodeParams {
   int32_t k;
   int32_t k_local;
   int32_t t;
-  float qk_scale;       // log2(e) / sqrt(D): logits are kept in the log2 domain
+  float qk_scale;       // log2(e) / sqrt(D) (times k_scale for E4M3 slots): log2-domain logits
+  float k_inv, v_inv;   // E4M3 slots: fl32(1 / k_scale), fl32(1 / v_scale)
+  float v_scale;        // E4M3 slots: the output is scaled by it once
 };
 
 // Eviction rankings (the C ABI's h2o_policy). The fp32 value a candidate is ranked by:
@@ -136,6 +138,7 @@ struct SeedParams {
   int32_t k_local;
   int32_t policy;       // seeding ranking, h2o_policy
   int32_t policy_param;
+  float k_inv, v_inv;   // E4M3 slots: fl32(1 / k_scale), fl32(1 / v_scale)
 };
 
 struct ResetParams {
@@ -165,13 +168,14 @@ size_t decode_scratch_bytes(int elem_bytes, int D, int k, int units);
 SplitScratch carve_decode_scratch(int elem_bytes, int D, int k, int units, void* scratch);
 
 hipError_t launch_reset(const ResetParams& p, hipStream_t s);
-hipError_t launch_decode(DType dt, int D, const DecodeParams& p, const SplitScratch& w,
+// f8: the slots hold E4M3 codes (fp16 / bf16 inputs only).
+hipError_t launch_decode(DType dt, bool f8, int D, const DecodeParams& p, const SplitScratch& w,
                          hipStream_t s);
 // fp16 / bf16 storage: MFMA kernels.
 hipError_t launch_prefill_attn_mfma(DType dt, int D, const PrefillParams& p, hipStream_t s);
 // fp32 storage: vector-ALU kernels.
 hipError_t launch_prefill_attn_f32(int D, const PrefillParams& p, hipStream_t s);
 hipError_t launch_prefill_colsum_f32(int D, const PrefillParams& p, hipStream_t s);
-hipError_t launch_seed(DType dt, int D, const SeedParams& p, hipStream_t s);
+hipError_t launch_seed(DType dt, bool f8, int D, const SeedParams& p, hipStream_t s);
 
 }  // namespace h2o

@@ -23,6 +23,9 @@
 // when they fit (T + k <= 15872 words); the seeded scores are then read back
 // from LDS.
 //
+// E4M3 slots (F8): each copied row is quantised on the way (x * 1/scale, clamped to +-448,
+// nearest-even E4M3 codes), 8 codes per 16-byte chunk of the prompt row.
+//
 // reset: slot_pos = -1, acc = 0 (blog §2.3: freeing a slot only marks it).
 #include "h2o_device.hpp"
 #include "h2o_kernels.hpp"
@@ -48,8 +51,10 @@ __device__ __forceinline__ unsigned wave_prefix(unsigned v, int lane) {
   return v;
 }
 
-template <typename T, int D>
+template <typename T, int D, bool F8>
 __global__ __launch_bounds__(kThreads) void seed_kernel(SeedParams p) {
+  using SC = SlotChunk<T, F8>;
+  using SE = typename SC::elem;
   extern __shared__ int lds_dyn[];               // [k] slot -> position, then [T] staged bits
   __shared__ unsigned hist[256];
   __shared__ unsigned wsum[kWaves];
@@ -70,8 +75,18 @@ __global__ __launch_bounds__(kThreads) void seed_kernel(SeedParams p) {
   constexpr int B = 4;                           // copies in flight per thread (more measured slower)
   const T* K = static_cast<const T*>(p.k) + (size_t)unit * Ts * D;
   const T* V = static_cast<const T*>(p.v) + (size_t)unit * Ts * D;
-  T* ks = static_cast<T*>(p.k_slots) + (size_t)unit * k * D;
-  T* vs = static_cast<T*>(p.v_slots) + (size_t)unit * k * D;
+  SE* ks = static_cast<SE*>(p.k_slots) + (size_t)unit * k * D;
+  SE* vs = static_cast<SE*>(p.v_slots) + (size_t)unit * k * D;
+  // A prompt chunk as the slot stores it.
+  auto put = [&](SE* dst_k, SE* dst_v, const uint4& kx, const uint4& vx) {
+    if constexpr (F8) {
+      SC::store(dst_k, quant_e4m3<T>(kx, p.k_inv));
+      SC::store(dst_v, quant_e4m3<T>(vx, p.v_inv));
+    } else {
+      SC::store(dst_k, kx);
+      SC::store(dst_v, vx);
+    }
+  };
   // Rows whose slot is known before the selection: every row when T <= k (slot = position),
   // else the recent window (positions T - k_local.., slots k_heavy..). Their first batch
   // of loads is issued now and lands while the column sums are formed.
@@ -96,8 +111,7 @@ __global__ __launch_bounds__(kThreads) void seed_kernel(SeedParams p) {
       if (idx < ftotal) {
         const int r = idx / CPR, ch = idx - r * CPR;
         const size_t dst = (size_t)(fdst + r) * D + ch * VEC;
-        st16(ks + dst, kf[i]);
-        st16(vs + dst, vf[i]);
+        put(ks + dst, vs + dst, kf[i], vf[i]);
       }
     }
   };
@@ -287,8 +301,7 @@ __global__ __launch_bounds__(kThreads) void seed_kernel(SeedParams p) {
       if (idx < total) {
         const int s = idx / CPR, ch = idx - s * CPR;
         const size_t dst = (size_t)s * D + ch * VEC;
-        st16(ks + dst, kr[i]);
-        st16(vs + dst, vr[i]);
+        put(ks + dst, vs + dst, kr[i], vr[i]);
       }
     }
   }
@@ -302,17 +315,21 @@ __global__ void reset_kernel(ResetParams p) {
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool F8 = false>
 hipError_t seed(const SeedParams& p, hipStream_t s) {
   const int k = p.k_heavy + p.k_local;
   const size_t lds = (size_t)k * sizeof(int) + (stage_alloc(p.T, k) ? (size_t)p.T * 4 : 0);
-  seed_kernel<T, D><<<dim3((unsigned)p.units), dim3(kThreads), lds, s>>>(p);
+  seed_kernel<T, D, F8><<<dim3((unsigned)p.units), dim3(kThreads), lds, s>>>(p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_seed(DType dt, int D, const SeedParams& p, hipStream_t s) {
+hipError_t launch_seed(DType dt, bool f8, int D, const SeedParams& p, hipStream_t s) {
+  if (f8) {
+    if (dt == DType::F16) return D == 64 ? seed<_Float16, 64, true>(p, s) : seed<_Float16, 128, true>(p, s);
+    return D == 64 ? seed<__bf16, 64, true>(p, s) : seed<__bf16, 128, true>(p, s);
+  }
   switch (dt) {
     case DType::F32: return D == 64 ? seed<float, 64>(p, s) : seed<float, 128>(p, s);
     case DType::F16: return D == 64 ? seed<_Float16, 64>(p, s) : seed<_Float16, 128>(p, s);

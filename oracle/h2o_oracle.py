@@ -174,7 +174,8 @@ def e4m3_decode(code) -> np.ndarray:
 def quantize_row(x, scale):
     """Codes and read-back values of a K or V row stored in an E4M3 slot (R14)."""
     s32 = np.float32(scale)
-    y = np.asarray(x, dtype=np.float32) * (np.float32(1.0) / s32)   # one fp32 rounding
+    with np.errstate(over="ignore"):   # a product past the fp32 range is +-inf, then saturates
+        y = np.asarray(x, dtype=np.float32) * (np.float32(1.0) / s32)   # one fp32 rounding
     r = e4m3_round(y)
     return e4m3_encode(r), r * float(s32)
 

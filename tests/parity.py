@@ -12,7 +12,7 @@ inputs and compares element by element:
     the GPU's choice and logs it;
   * attention outputs: max abs error <= 2e-3 (fp16 / bf16) or 1e-5 (fp32);
   * scores (acc_score, column sums, evicted scores): 1e-4 relative;
-  * K/V slot rows: bit-exact (they are copies of the inputs).
+  * K/V slot rows: bit-exact (copies of the inputs, or their E4M3 codes).
 """
 from __future__ import annotations
 
@@ -32,7 +32,7 @@ def run_gpu(w, x, record_steps=True):
     B, H, d, T, n = w.batch, w.heads, w.head_dim, w.prompt, w.steps
     dev = x["q_dec"].device if n else x["q_prompt"].device
     cache = H2OCache(B, H, d, w.k_heavy, w.k_local, w.torch_dtype, dev, max_prompt=T,
-                     policy=w.policy, policy_param=w.policy_param)
+                     **w.cache_kw)
     cache.reset()
     r = {}
     if T > 0:
@@ -64,7 +64,7 @@ def run_gpu_ragged(w, x, lens):
     B, H, d, T, n = w.batch, w.heads, w.head_dim, w.prompt, w.steps
     dev = x["q_prompt"].device
     cache = H2OCache(B, H, d, w.k_heavy, w.k_local, w.torch_dtype, dev, max_prompt=T,
-                     policy=w.policy, policy_param=w.policy_param)
+                     **w.cache_kw)
     cache.reset()
     lens_d = torch.tensor(lens, dtype=torch.int32, device=dev)
     r = {}
@@ -137,8 +137,7 @@ def check_unit(w, x, r, b, h, steps=None, prompt_len=None):
     u["Qp"], u["Kp"], u["Vp"] = u["Qp"][:T], u["Kp"][:T], u["Vp"][:T]
     pos0 = r["pos0"][b, h].cpu().numpy()
     acc0 = r["acc0"][b, h].cpu().numpy()
-    cache = UnitCache(w.k_heavy, w.k_local, w.head_dim, policy=w.policy,
-                      policy_param=w.policy_param)
+    cache = UnitCache(w.k_heavy, w.k_local, w.head_dim, **w.cache_kw)
     err = {"prefill_out": 0.0, "decode_out": 0.0, "colsum_rel": 0.0, "acc_rel": 0.0}
     if T > 0:
         kept_gpu = sorted(int(p) for p in pos0 if p >= 0)
@@ -180,10 +179,16 @@ def check_unit(w, x, r, b, h, steps=None, prompt_len=None):
         err["acc_rel"] = float((np.abs(gacc - cache.acc) / np.maximum(np.abs(cache.acc), 1e-30)).max())
         assert ok.all(), f"unit ({b},{h}) final acc differs at slots {np.nonzero(~ok)[0][:5]}"
         valid = cache.pos >= 0
-        gk = r["cache"].k_slots[b, h].double().cpu().numpy()
-        gv = r["cache"].v_slots[b, h].double().cpu().numpy()
-        assert np.array_equal(gk[valid], cache.K[valid]), f"unit ({b},{h}) K slots differ"
-        assert np.array_equal(gv[valid], cache.V[valid]), f"unit ({b},{h}) V slots differ"
+        if w.slot_format == "e4m3":           # the stored codes, byte for byte
+            gk = r["cache"].k_slots[b, h].view(torch.uint8).cpu().numpy()
+            gv = r["cache"].v_slots[b, h].view(torch.uint8).cpu().numpy()
+            ek, ev = cache.Kc, cache.Vc
+        else:
+            gk = r["cache"].k_slots[b, h].double().cpu().numpy()
+            gv = r["cache"].v_slots[b, h].double().cpu().numpy()
+            ek, ev = cache.K, cache.V
+        assert np.array_equal(gk[valid], ek[valid]), f"unit ({b},{h}) K slots differ"
+        assert np.array_equal(gv[valid], ev[valid]), f"unit ({b},{h}) V slots differ"
     err["ties"] = list(cache.ties)
     return err
 

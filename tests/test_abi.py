@@ -80,6 +80,13 @@ def test_workspace_bytes():
     (dict(policy=-1), h2o.H2O_ERR_INVALID),
     (dict(policy=2, policy_param=0), h2o.H2O_ERR_INVALID),
     (dict(policy=1, policy_param=-1), h2o.H2O_ERR_INVALID),
+    (dict(slot_format=2), h2o.H2O_ERR_INVALID),
+    (dict(slot_format=-1), h2o.H2O_ERR_INVALID),
+    (dict(slot_format=1, dtype=h2o.H2O_F32, k_scale=1.0, v_scale=1.0), h2o.H2O_ERR_UNSUPPORTED),
+    (dict(slot_format=1, k_scale=0.0, v_scale=1.0), h2o.H2O_ERR_INVALID),
+    (dict(slot_format=1, k_scale=1.0, v_scale=-2.0), h2o.H2O_ERR_INVALID),
+    (dict(slot_format=1, k_scale=float("inf"), v_scale=1.0), h2o.H2O_ERR_INVALID),
+    (dict(slot_format=1, k_scale=1.0, v_scale=float("nan")), h2o.H2O_ERR_INVALID),
 ])
 def test_descriptor_checks(kw, status):
     d = desc(**kw)
@@ -87,6 +94,18 @@ def test_descriptor_checks(kw, status):
     assert h2o.h2o_last_error() != ""
     assert h2o.h2o_decode_step(d, 5, A, A, A, A, None, 0, 0, 0) == status
     assert h2o.h2o_prefill(d, A, A, A, 8, A, 0, A, 1 << 20, 0) == status
+
+
+def test_e4m3_slots_take_the_input_dtype_workspace():
+    # E4M3 slots change the row bytes, not the launch plan: the workspace is the same.
+    for dt in (h2o.H2O_F16, h2o.H2O_BF16):
+        for kh in (4, 300, 3000):
+            a = desc(dtype=dt, k_heavy=kh)
+            b = desc(dtype=dt, k_heavy=kh, slot_format=1, k_scale=0.5, v_scale=2.0)
+            for T in (0, 100, 1000):
+                assert h2o.h2o_workspace_bytes(b, T) == h2o.h2o_workspace_bytes(a, T) > 0 or T == 0
+    # scales are not read for slots in the input dtype
+    assert h2o.h2o_workspace_bytes(desc(k_scale=0.0, v_scale=float("nan")), 16) > 0
 
 
 def test_null_descriptor():

@@ -377,3 +377,95 @@ def test_prefill_exact_ties_keep_the_newest():
     kept = sorted(int(p) for p in r["pos0"][0, 0].cpu() if p >= 0)
     assert kept == sorted(sorted(live) + dead[-10:] + list(range(w.prompt - w.k_local, w.prompt)))
     check_units(w, x, r, range(w.units_per_layer))
+
+
+# E4M3 slots (the oracle's reading R14): every row that enters a slot is stored as FP8 E4M3
+# codes; the codes must match the oracle's byte for byte and the outputs its attention over
+# the read-back values.
+E4M3_CASES = [
+    # resident decode (256 threads), unit scales
+    Workload(78, "e4m3-f16-d128", 2, 1, 3, 128, "f16", 200, 40, 24, 16, heavy_frac=0.05,
+             slot_format="e4m3"),
+    # bf16 d=64, scales that are not powers of two
+    Workload(77, "e4m3-bf16-d64-scaled", 2, 1, 3, 64, "bf16", 200, 40, 24, 16, heavy_frac=0.05,
+             slot_format="e4m3", k_scale=0.37, v_scale=1.9),
+    # scales so small that a few percent of the elements saturate at +-448
+    Workload(76, "e4m3-f16-saturating", 2, 1, 2, 128, "f16", 150, 30, 20, 12,
+             heavy_frac=0.05, slot_format="e4m3", k_scale=0.004, v_scale=0.003),
+    # a prompt shorter than k (every position kept) that the decode steps then fill and
+    # overflow, and an empty prompt
+    Workload(75, "e4m3-bf16-fill", 2, 1, 2, 128, "bf16", 10, 50, 20, 20, slot_format="e4m3",
+             k_scale=0.5, v_scale=0.25),
+    Workload(74, "e4m3-f16-empty-prompt", 1, 1, 3, 64, "f16", 0, 40, 12, 12,
+             slot_format="e4m3"),
+    # the 1024-thread resident decode (k = 300) and the split decode (k = 600), with Top-K
+    Workload(73, "e4m3-f16-k300", 1, 1, 2, 128, "f16", 360, 30, 150, 150, heavy_frac=0.05,
+             slot_format="e4m3", k_scale=0.75, v_scale=0.6),
+    Workload(72, "e4m3-bf16-split", 1, 1, 2, 128, "bf16", 700, 30, 300, 300, heavy_frac=0.05,
+             slot_format="e4m3", k_scale=1.3),
+    Workload(71, "e4m3-f16-split-topk", 1, 1, 2, 128, "f16", 650, 24, 320, 280,
+             slot_format="e4m3", policy="topk"),
+]
+
+
+@pytest.mark.parametrize("w", E4M3_CASES, ids=[w.name for w in E4M3_CASES])
+def test_e4m3_slots(w):
+    announce(f"[parity] {w.name}: E4M3 slots, scales {w.k_scale}/{w.v_scale}, "
+             f"k = {w.k_heavy}+{w.k_local}")
+    x = gen(w)
+    r = run_gpu(w, x)
+    assert r["cache"].k_slots.dtype == torch.float8_e4m3fn
+    agg = check_units(w, x, r, range(w.units_per_layer))
+    announce(f"[parity] {w.name}: prefill {agg['prefill_out']:.2e} decode {agg['decode_out']:.2e} "
+             f"ties={len(agg['ties'])}")
+
+
+def test_e4m3_ragged_batch():
+    from tests.parity import run_gpu_ragged
+    lens = [120, 0, 33, 64]
+    w = Workload(70, "e4m3-ragged-f16", len(lens), 1, 2, 128, "f16", max(lens), 20, 24, 16,
+                 heavy_frac=0.05, slot_format="e4m3", k_scale=0.8, v_scale=1.1)
+    announce(f"[parity] {w.name}: prompt lengths {lens}")
+    x = gen(w)
+    r = run_gpu_ragged(w, x, lens)
+    check_units(w, x, r, range(w.units_per_layer), lens=lens)
+
+
+def _all_finite_half(dtype):
+    bits = torch.arange(1 << 16, dtype=torch.int32).to(torch.int16)
+    x = bits.view(torch.float16 if dtype == "f16" else torch.bfloat16)
+    return x[torch.isfinite(x)]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("scale", [1.0, 0.37])
+def test_e4m3_quantisation_of_every_half_value(dtype, scale):
+    # Every finite fp16 / bf16 value enters a slot once, as the new token of a decode step
+    # on an empty cache (it takes slot 0): the codes must equal the oracle's.
+    from kv_cache_eviction_03_amd import H2OCache
+    from oracle import quantize_row
+    vals = _all_finite_half(dtype)
+    d = 128
+    units = (vals.numel() + d - 1) // d
+    pad = units * d - vals.numel()
+    row = torch.cat([vals, torch.zeros(pad, dtype=vals.dtype)]).reshape(1, units, d)
+    announce(f"[parity] e4m3 quantisation: {vals.numel()} finite {dtype} values, scale {scale}")
+    dev = "cuda"
+    tdt = row.dtype
+    c = H2OCache(1, units, d, 2, 2, tdt, dev, slot_format="e4m3", k_scale=scale,
+                 v_scale=scale)
+    c.reset()
+    kn = row.to(dev)
+    vn = row.flip(-1).contiguous().to(dev)
+    q = torch.zeros_like(kn)
+    c.decode(q, kn, vn)
+    torch.cuda.synchronize()
+    gk = c.k_slots[0, :, 0].view(torch.uint8).cpu().numpy()
+    gv = c.v_slots[0, :, 0].view(torch.uint8).cpu().numpy()
+    ek, _ = quantize_row(row.double().numpy().reshape(-1), scale)
+    ev, _ = quantize_row(row.flip(-1).double().numpy().reshape(-1), scale)
+    assert np.array_equal(gk.reshape(-1), ek), \
+        f"{int((gk.reshape(-1) != ek).sum())} K codes differ"
+    assert np.array_equal(gv.reshape(-1), ev), \
+        f"{int((gv.reshape(-1) != ev).sum())} V codes differ"
+    assert c.slot_pos[0, :, 0].cpu().tolist() == [0] * units

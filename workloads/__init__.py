@@ -53,6 +53,15 @@ class Workload:
     sinks: int = 0
     policy: str = "h2o"       # eviction ranking the cache runs with (h2o, sinks, strided, topk)
     policy_param: int = 0
+    slot_format: str = "input"   # K/V slot storage: the input dtype, or "e4m3" codes
+    k_scale: float = 1.0         # E4M3 scales of K and V
+    v_scale: float = 1.0
+
+    @property
+    def cache_kw(self) -> dict:
+        """Cache options shared by the library's H2OCache and the oracle's UnitCache."""
+        return dict(policy=self.policy, policy_param=self.policy_param,
+                    slot_format=self.slot_format, k_scale=self.k_scale, v_scale=self.v_scale)
 
     @property
     def k(self) -> int:
