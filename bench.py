@@ -32,6 +32,7 @@ Timing:
   * hbm_measured_ceiling: context only, plain PyTorch streaming read and copy rates;
   * ragged_step: the bench layer with seeded prompt lengths in [256, 512] through the
     ragged entry points, against the same batch padded to 512;
+  * decode_by_workload_e4m3: the same shapes with FP8 E4M3 slots (half the slot bytes);
   * decode_by_policy: the bench layer's decode launch under each eviction ranking;
   * llama_stack_decode: the LLaMA-7B-shaped model's decode step, 32 layers each with
     its own prefilled cache (3.69 GB of slots per step, far beyond the MALL);
@@ -80,9 +81,11 @@ def decode_traffic():
 
 
 def decode_bytes_per_unit(w) -> int:
-    """Algorithmic HBM bytes of one decode step of one unit."""
+    """Algorithmic HBM bytes of one decode step of one unit (slots of one byte per element
+    when they hold E4M3 codes; q, k_new and v_new always in the input dtype)."""
     k, d, s = w.k, w.head_dim, w.elem_bytes
-    return 2 * k * d * s + 12 * k + 3 * d * s + 4 * d + 2 * d * s + 8
+    ss = 1 if w.slot_format == "e4m3" else s
+    return 2 * k * d * ss + 12 * k + 3 * d * s + 4 * d + 2 * d * ss + 8
 
 
 def prefill_flops_per_unit(w) -> int:
@@ -178,12 +181,14 @@ def decode_by_policy(n=32, reps=5):
     return res
 
 
-def decode_by_workload(ids=(2, 3, 4, 5), n=32, reps=5):
+def decode_by_workload(ids=(2, 3, 4, 5), n=32, reps=5, slot_format="input"):
     """Decode launches of each workload's layer shape, graph-replayed, timed with HIP events.
 
     The cache is filled by a prefill of k + 64 tokens (so every step evicts), then n
     decode steps are captured once and replayed; the best replay's mean per launch is
-    reported with the algorithmic bytes of one launch.
+    reported with the algorithmic bytes of one launch. slot_format "e4m3" runs the same
+    shapes with FP8 E4M3 slots (scales 1: the synthetic K/V, heavy-hitter keys included,
+    stay far inside the E4M3 range of +-448).
     """
     import torch
 
@@ -192,10 +197,11 @@ def decode_by_workload(ids=(2, 3, 4, 5), n=32, reps=5):
     dev = "cuda:0"
     res = []
     for wid in ids:
-        w = WORKLOADS[wid].scaled(prompt=WORKLOADS[wid].k + 64, steps=n, layers=1)
+        w = WORKLOADS[wid].scaled(prompt=WORKLOADS[wid].k + 64, steps=n, layers=1,
+                                  slot_format=slot_format)
         x = generate(w, seed=0, device=dev)
         c = H2OCache(w.batch, w.heads, w.head_dim, w.k_heavy, w.k_local, w.torch_dtype, dev,
-                     max_prompt=w.prompt)
+                     max_prompt=w.prompt, **w.cache_kw)
         out = torch.empty((n, w.batch, w.heads, w.head_dim), dtype=torch.float32, device=dev)
         c.reset()
         c.prefill(x["q_prompt"], x["k_prompt"], x["v_prompt"])
@@ -219,8 +225,9 @@ def decode_by_workload(ids=(2, 3, 4, 5), n=32, reps=5):
             us = 1e3 * a.elapsed_time(b) / n
             best = us if best is None else min(best, us)
         byt = decode_bytes_per_unit(w) * w.units_per_layer
+        slots = "e4m3 slots" if slot_format == "e4m3" else f"{w.dtype} slots"
         res.append({"workload": f"{w.name} layer: B {w.batch}, H {w.heads}, d {w.head_dim}, "
-                                f"{w.dtype}, k = {w.k_heavy}+{w.k_local}",
+                                f"{w.dtype} inputs, {slots}, k = {w.k_heavy}+{w.k_local}",
                     "us_per_launch": best, "algorithmic_MB": byt / 1e6,
                     "GBps": byt / (best * 1e-6) / 1e9, "hbm_frac": byt / (best * 1e-6) / 1e9 / HBM_PEAK_GBS,
                     "decode_tokens_per_s": w.batch / (best * 1e-6)})
@@ -664,6 +671,8 @@ def main():
     if args.decode_shapes:
         for r in decode_by_workload():
             print(json.dumps(r), flush=True)
+        for r in decode_by_workload(slot_format="e4m3"):
+            print(json.dumps(r), flush=True)
         return
     if args.stream_only:
         print(json.dumps(stream_sustained()), flush=True)
@@ -831,6 +840,7 @@ def main():
         result["prefill_mfma_opt30b"] = prefill_mfma_probe()
     if not args.no_decode_shapes:
         result["decode_by_workload"] = decode_by_workload()
+        result["decode_by_workload_e4m3"] = decode_by_workload(slot_format="e4m3")
     if not args.no_cold:
         result["hbm_measured_ceiling"] = hbm_ceiling()
         result["roofline_cold"] = decode_cold(w)
