@@ -30,6 +30,8 @@ Timing:
   * dense_comparator: context only, the same decode steps with k = T + n (nothing
     evicted) against the H2O budget;
   * hbm_measured_ceiling: context only, plain PyTorch streaming read and copy rates;
+  * launch_floor: context only, the per-launch time of graph-replayed trivial kernels,
+    and the decode launch's bandwidth over the time it spends above that floor;
   * ragged_step: the bench layer with seeded prompt lengths in [256, 512] through the
     ragged entry points, against the same batch padded to 512;
   * decode_by_workload_e4m3: the same shapes with FP8 E4M3 slots (half the slot bytes);
@@ -419,6 +421,42 @@ def decode_cold(w, replicas=36, reps=5):
             "algorithmic_bytes_per_launch": byt, "replicas": replicas,
             "state_swept_MB": replicas * byt / 1e6,
             "duration_from": "HIP events around graph replays of one launch per replica (median)"}
+
+
+def launch_floor(w, n=32, reps=10):
+    """Context: the per-launch time of graph-replayed kernels that do almost nothing (a
+    one-element torch fill, one workgroup; the library's h2o_reset of the bench layer,
+    104 workgroups writing 0.2 MB), i.e. the dispatch cost any kernel in a graph pays."""
+    import torch
+
+    from kv_cache_eviction_03_amd import H2OCache
+    dev = "cuda:0"
+    x = torch.empty(1, device=dev)
+    c = H2OCache(w.batch, w.heads, w.head_dim, w.k_heavy, w.k_local, w.torch_dtype, dev)
+    res = {}
+    for name, fn in (("fill_1_workgroup_us", x.zero_), ("h2o_reset_us", c.reset)):
+        fn()
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream(dev)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for _ in range(n):
+                    fn()
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            us = 1e3 * a.elapsed_time(b) / n
+            best = us if best is None else min(best, us)
+        res[name] = best
+        del g
+    del x, c
+    return res
 
 
 def hbm_ceiling(reps=10):
@@ -836,6 +874,11 @@ def main():
         },
         "wall_s_timed_loop": wall,
     }
+    floor = launch_floor(w)
+    above = dec_kernel_us - floor["h2o_reset_us"]
+    floor["decode_us_above_floor"] = above
+    floor["decode_GBps_above_floor"] = dec_bytes / (above * 1e-6) / 1e9 if above > 0 else None
+    result["launch_floor"] = floor
     if not args.no_mfma_probe:
         result["prefill_mfma_opt30b"] = prefill_mfma_probe()
     if not args.no_decode_shapes:

@@ -166,11 +166,17 @@ __global__ __launch_bounds__(kThreads) void seed_kernel(SeedParams p) {
     n_keep = T_;
     for (int s = tid; s < T_; s += kThreads) slot_of[s] = s;
   } else {
+    // The selection reads the column sums from the LDS stage or from global memory; the
+    // two are separate instantiations, so every read is a plain LDS or global load (a
+    // runtime choice between the two pointers would make them generic-address loads).
+    auto select = [&](auto from_lds) -> int {
+    constexpr bool kLds = decltype(from_lds)::value;
     const int ncand = T_ - p.k_local;
     // The ranking score of position j: the column sum under H2O and Top-K, a 0/1 position
     // class under the position policies.
     auto key = [&](int j) -> unsigned {
-      const float cj = staged ? __uint_as_float(bits[j]) : c[j];
+      float cj;
+      if constexpr (kLds) cj = __uint_as_float(bits[j]); else cj = c[j];
       return __float_as_uint(policy_seed(p.policy, p.policy_param, cj, j));
     };
 
@@ -267,22 +273,28 @@ __global__ __launch_bounds__(kThreads) void seed_kernel(SeedParams p) {
       running += total;
       __syncthreads();
     }
-    n_keep = running < k ? running : k;
+    return running < k ? running : k;
+    };
+    n_keep = staged ? select(std::true_type{}) : select(std::false_type{});
   }
   __syncthreads();
 
   int32_t* pos = p.slot_pos + (size_t)unit * k;
   float* acc = p.acc + (size_t)unit * k;
-  for (int s = tid; s < k; s += kThreads) {
-    if (s < n_keep) {
-      const int j = slot_of[s];
-      pos[s] = j;
-      acc[s] = staged ? __uint_as_float(bits[j]) : c[j];
-    } else {
-      pos[s] = -1;
-      acc[s] = 0.f;
+  auto write_meta = [&](auto from_lds) {
+    for (int s = tid; s < k; s += kThreads) {
+      if (s < n_keep) {
+        const int j = slot_of[s];
+        pos[s] = j;
+        if constexpr (decltype(from_lds)::value) acc[s] = __uint_as_float(bits[j]);
+        else acc[s] = c[j];
+      } else {
+        pos[s] = -1;
+        acc[s] = 0.f;
+      }
     }
-  }
+  };
+  if (staged) write_meta(std::true_type{}); else write_meta(std::false_type{});
   // The heavy rows (slots [0, k_heavy) when T > k), gathered by the selection.
   const int total = (T_ > k ? p.k_heavy : 0) * CPR;
   for (int base = 0; base < total; base += B * kThreads) {
