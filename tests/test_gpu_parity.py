@@ -186,6 +186,22 @@ def test_opt30b_layer_fp16_sampled_units(seed):
              f"ties={len(agg['ties'])}")
 
 
+@pytest.mark.parametrize("wid,n_units", [(3, 8), (4, 6)])
+def test_e4m3_full_layer_shapes_sampled_units(wid, n_units):
+    # The LLaMA-7B and OPT-30B layer shapes with E4M3 slots, in the launch configurations
+    # the E4M3 decode timings use (256-thread and 1024-thread resident decode).
+    w = WORKLOADS[wid].scaled(slot_format="e4m3")
+    announce(f"[parity] {w.name} e4m3 slots: full shape, {n_units} sampled units")
+    x = gen(w)
+    r = run_gpu(w, x)
+    assert r["cache"].k_slots.dtype == torch.float8_e4m3fn
+    agg = check_units(w, x, r, sample_units(w.units_per_layer, n_units, seed=wid))
+    announce(f"[parity] {w.name} e4m3: prefill {agg['prefill_out']:.2e} decode "
+             f"{agg['decode_out']:.2e} ties={len(agg['ties'])}")
+    del x, r
+    torch.cuda.empty_cache()
+
+
 def test_determinism_bitwise():
     w = WORKLOADS[2]
     announce(f"[determinism] {w.name} twice")
