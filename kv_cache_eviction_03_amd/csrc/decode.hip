@@ -194,8 +194,12 @@ __device__ __forceinline__ uint64_t score_key(float a, int pos) {
 template <typename T, int D, int THREADS, bool F8>
 // Register budget: at most 128 VGPRs for the 256-thread shape, so that at least four
 // workgroups share a CU (three per CU measured 3.5% slower on the 32-layer LLaMA-7B-shaped
-// stack). The kernels currently need about 92.
-__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(THREADS == 256 ? 4 : 1, 8)))
+// stack). The kernels currently need about 92. The 1024-thread E4M3 shape is held to 64
+// (eight waves per SIMD, two workgroups per CU; about four VGPRs spill): 29.1 -> 27.2 us on
+// the OPT-30B layer. The same cap on the 256-thread E4M3 shape measured slower (12.5 ->
+// 15.8 us on the LLaMA-7B layer), and the fp16 / bf16 shapes need about 92.
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(
+    THREADS == 256 ? 4 : (F8 ? 8 : 1), 8)))
 void decode_resident_kernel(DecodeParams p) {
   using S = Shape<T, D, THREADS>;
   using SC = SlotChunk<T, F8>;
