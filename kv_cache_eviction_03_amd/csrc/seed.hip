@@ -41,13 +41,17 @@ constexpr int kStageWords = 62 * 1024 / 4;
 __host__ __device__ inline bool stage_alloc(int Ts, int k) { return Ts + k <= kStageWords; }
 __host__ __device__ inline bool stage_bits(int Ts, int Tb, int k) { return Tb > k && stage_alloc(Ts, k); }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ unsigned wave_prefix(unsigned v, int lane) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const unsigned u = __shfl_up(v, o, kWave);
-    if (lane >= o) v += u;
-  }
+// Inclusive prefix sum over the 64 lanes of a wave, with DPP lane moves only: shifts by
+// 1, 2, 4 and 8 inside each 16-lane row (lanes shifted in from outside the row read 0),
+// then row_bcast:15 adds the last lane of rows 0 and 2 to rows 1 and 3, and row_bcast:31
+// the last lane of row 1 to rows 2 and 3.
+__device__ __forceinline__ unsigned wave_prefix(unsigned v) {
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true);   // row_shr:1
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true);   // row_shr:2
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true);   // row_shr:4
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true);   // row_shr:8
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return v;
 }
 
@@ -56,7 +60,7 @@ __global__ __launch_bounds__(kThreads) void seed_kernel(SeedParams p) {
   using SC = SlotChunk<T, F8>;
   using SE = typename SC::elem;
   extern __shared__ int lds_dyn[];               // [k] slot -> position, then [T] staged bits
-  __shared__ unsigned hist[256];
+  __shared__ unsigned hist[2][256];             // radix passes alternate between the two
   __shared__ unsigned wsum[kWaves];
   __shared__ unsigned s_sel, s_above;
   __shared__ int wcnt[2][kWaves];
@@ -182,9 +186,12 @@ __global__ __launch_bounds__(kThreads) void seed_kernel(SeedParams p) {
 
     unsigned prefix = 0, mask = 0, want = (unsigned)p.k_heavy, eq_total = 0;
     if (p.k_heavy > 0) {
+      hist[1][tid] = 0;                          // the first pass counts into hist[1]
       for (int pass = 3; pass >= 0; --pass) {
         const int sh = pass * 8;
-        hist[tid] = 0;
+        unsigned* h = hist[pass & 1];
+        // h was cleared during the previous pass (or above), and every read of it by the
+        // pass that used it last came before the barrier that ended its counting loop.
         __syncthreads();
         for (int j0 = 0; j0 < ncand; j0 += kThreads) {
           const int j = j0 + tid;
@@ -202,16 +209,17 @@ __global__ __launch_bounds__(kThreads) void seed_kernel(SeedParams p) {
             const int leader = __builtin_ctzll(pend);
             const unsigned lb = (unsigned)__builtin_amdgcn_readlane((int)bin, leader);
             const uint64_t same = __ballot(bin == lb) & pend;
-            if (lane == leader) atomicAdd(&hist[lb], (unsigned)__popcll(same));
+            if (lane == leader) atomicAdd(&h[lb], (unsigned)__popcll(same));
             pend &= ~same;
           }
-          if ((pend >> lane) & 1ull) atomicAdd(&hist[bin], 1u);
+          if ((pend >> lane) & 1ull) atomicAdd(&h[bin], 1u);
         }
         __syncthreads();
         // Thread i holds bin 255 - i, so a prefix over threads is a suffix over bins.
-        const unsigned cnt = hist[255 - tid];
-        const unsigned incl_w = wave_prefix(cnt, lane);
+        const unsigned cnt = h[255 - tid];
+        const unsigned incl_w = wave_prefix(cnt);
         if (lane == 63) wsum[wave] = incl_w;
+        hist[(pass & 1) ^ 1][tid] = 0;           // the next pass's histogram
         __syncthreads();
         unsigned before = 0;
 #pragma unroll
@@ -225,9 +233,11 @@ __global__ __launch_bounds__(kThreads) void seed_kernel(SeedParams p) {
         prefix |= s_sel << sh;
         mask |= 255u << sh;
         want -= s_above;
-        if (pass == 0) eq_total = hist[s_sel];
-        __syncthreads();
+        if (pass == 0) eq_total = h[s_sel];
+        // No barrier here: the next pass writes s_sel, s_above and wsum only after two
+        // barriers that every thread reaches after these reads.
       }
+      __syncthreads();                           // s_sel / s_above reads done before reuse
     }
     // Keep: j >= ncand (recent window); bits > v*; bits == v* and among the `want`
     // newest such positions (want = how many equal ones are still needed).
