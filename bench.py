@@ -39,7 +39,9 @@ Timing:
   * llama_stack_decode: the LLaMA-7B-shaped model's decode step, 32 layers each with
     its own prefilled cache (3.69 GB of slots per step, far beyond the MALL);
   * stream_sustained: the long-streaming workload in full (4096 slots, 2^20 decode
-    steps from an empty cache), device time per 65,536-step window after the fill.
+    steps from an empty cache), device time per 65,536-step window after the fill; then
+    (graph_replayed) its first 4096 + 4 x 65,536 steps again as replays of one 256-step
+    HIP graph that advances its own positions, checked bit for bit against the direct run.
 """
 from __future__ import annotations
 
@@ -542,13 +544,20 @@ def dense_comparator(w, reps=5):
             "decode_us_per_step": best, "decode_tokens_per_s": w.batch / (best * 1e-6)}
 
 
-def stream_sustained(window=65536):
+def stream_sustained(window=65536, graph_windows=4, G=256):
     """The long-streaming workload in full: 32 heads, 4096 slots, 2^20 decode steps of
     seeded inputs (2% heavy-hitter keys), one h2o_decode_step call per step through the C
     ABI (t is a host argument, so the steps cannot be one replayed graph). HIP events at
     window boundaries give the device time of the 4096 fill steps and of each 65,536-step
     window after them; the host's own time per enqueued step is reported beside it, to
-    show the loop is bound by the GPU, not by the enqueueing."""
+    show the loop is bound by the GPU, not by the enqueueing.
+
+    Then the same stream through graphs: the ragged entry point takes each step's position
+    from device memory, so one HIP graph holds G steps (a gather of the G steps' inputs by
+    position, G decode launches, and an add that advances the positions by G) and is
+    replayed with no host work per step. It runs the fill and `graph_windows` windows from
+    an empty cache, and its final cache state is compared bit for bit with the direct
+    run's state at the same step."""
     import ctypes
     import torch
     from kv_cache_eviction_03_amd import H2OCache
@@ -574,6 +583,9 @@ def stream_sustained(window=65536):
     if marks[-1] < n:
         marks.append(n)                         # a last, shorter window
     events = {}
+    snap_at = k + graph_windows * window
+    names = ("k_slots", "v_slots", "slot_pos", "acc_score")
+    snap = None
     torch.cuda.synchronize()
     host0 = time.perf_counter()
     t = 0
@@ -585,6 +597,8 @@ def stream_sustained(window=65536):
             st = fn(dref, t, q0 + t * sb, k0 + t * sb, v0 + t * sb, op, None, wp, wn, sp)
             if st:
                 raise RuntimeError(f"h2o_decode_step failed at t = {t}: {lib.h2o_last_error()}")
+        if b == snap_at:
+            snap = {nm: getattr(c, nm).clone() for nm in names}
     e = torch.cuda.Event(enable_timing=True)
     e.record(stream)
     events[marks[-1]] = e
@@ -616,8 +630,63 @@ def stream_sustained(window=65536):
                 "+ 8 per unit; the host waits on a full launch queue, so its time per step "
                 "matches the device's",
     }
-    del x, c, out
+    if snap is not None and snap_at % G == 0 and window % G == 0 and k % G == 0:
+        res["graph_replayed"] = stream_graph(w, x, snap, snap_at, k, window, G)
+    del x, c, out, snap
     torch.cuda.empty_cache()
+    return res
+
+
+def stream_graph(w, x, snap, steps, fill, window, G):
+    """The stream's first `steps` decode steps as replays of one G-step HIP graph (see
+    stream_sustained), timed per window with HIP events; checked bit for bit against the
+    direct run's cache state at the same step."""
+    import torch
+    from kv_cache_eviction_03_amd import H2OCache
+    dev = "cuda:0"
+    B, H, d = w.batch, w.heads, w.head_dim
+    c = H2OCache(B, H, d, w.k_heavy, w.k_local, w.torch_dtype, dev)
+    c.reset()
+    tp = torch.arange(G, dtype=torch.int32, device=dev)        # positions of the G steps
+    qs, ks, vs = (torch.empty((G, B, H, d), dtype=w.torch_dtype, device=dev) for _ in range(3))
+    out = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            torch.index_select(x["q_dec"], 0, tp, out=qs)
+            torch.index_select(x["k_dec"], 0, tp, out=ks)
+            torch.index_select(x["v_dec"], 0, tp, out=vs)
+            for i in range(G):
+                c.decode_ragged(qs[i], ks[i], vs[i], out=out, t=tp[i:i + 1])
+            tp.add_(G)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    marks = [0, fill] + list(range(fill + window, steps + 1, window))
+    ev = []
+    for a, b in zip(marks[:-1], marks[1:]):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range((b - a) // G):
+            g.replay()
+        e1.record(stream)
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    for nm in ("k_slots", "v_slots", "slot_pos", "acc_score"):
+        if not torch.equal(getattr(c, nm), snap[nm]):
+            raise RuntimeError(f"graph-replayed stream diverged from the direct run in {nm}")
+    us = [m * 1e3 / window for m in ms[1:]]
+    step_bytes = decode_bytes_per_unit(w) * w.units_per_layer
+    res = {"steps": steps, "graph_steps": G, "replays": steps // G,
+           "fill_ms": ms[0], "windows": len(us),
+           "us_per_step_window_min": min(us), "us_per_step_window_max": max(us),
+           "tokens_per_s_sustained": (steps - fill) * B / (sum(ms[1:]) * 1e-3),
+           "hbm_frac_sustained": step_bytes * (steps - fill) / (sum(ms[1:]) * 1e-3) / 1e9
+           / HBM_PEAK_GBS,
+           "matches_direct_run": True}
+    del g, c, qs, ks, vs, out, tp
     return res
 
 
