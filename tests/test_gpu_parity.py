@@ -202,6 +202,53 @@ def test_e4m3_full_layer_shapes_sampled_units(wid, n_units):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("slot_format", ["input", "e4m3"])
+def test_graph_replayed_stream_matches_eager(slot_format):
+    # A stream with no prompt through the split decode (k = 600), once step by step and once
+    # as replays of a 64-step HIP graph that gathers its inputs by position, decodes, and
+    # advances its own device positions. Same cache state and outputs, bit for bit.
+    from kv_cache_eviction_03_amd import H2OCache
+    w = Workload(69, "graph-stream-bf16", 1, 1, 3, 128, "bf16", 0, 768, 300, 300,
+                 heavy_frac=0.02, slot_format=slot_format)
+    G = 64
+    announce(f"[graph] {w.name} {slot_format}: {w.steps} steps, eager vs {G}-step graph replays")
+    x = gen(w)
+    B, H, d = w.batch, w.heads, w.head_dim
+    names = ("k_slots", "v_slots", "slot_pos", "acc_score")
+    a = H2OCache(B, H, d, w.k_heavy, w.k_local, w.torch_dtype, "cuda", **w.cache_kw)
+    a.reset()
+    outs_a = torch.empty((w.steps, B, H, d), dtype=torch.float32, device="cuda")
+    for t in range(w.steps):
+        a.decode(x["q_dec"][t], x["k_dec"][t], x["v_dec"][t], out=outs_a[t])
+    b = H2OCache(B, H, d, w.k_heavy, w.k_local, w.torch_dtype, "cuda", **w.cache_kw)
+    b.reset()
+    tp = torch.arange(G, dtype=torch.int32, device="cuda")
+    qs, ks, vs = (torch.empty((G, B, H, d), dtype=w.torch_dtype, device="cuda") for _ in range(3))
+    outs_b = torch.empty((w.steps, B, H, d), dtype=torch.float32, device="cuda")
+    stage = torch.empty((G, B, H, d), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            torch.index_select(x["q_dec"], 0, tp, out=qs)
+            torch.index_select(x["k_dec"], 0, tp, out=ks)
+            torch.index_select(x["v_dec"], 0, tp, out=vs)
+            for i in range(G):
+                b.decode_ragged(qs[i], ks[i], vs[i], out=stage[i], t=tp[i:i + 1])
+            tp.add_(G)
+    torch.cuda.synchronize()
+    for r in range(w.steps // G):
+        g.replay()
+        torch.cuda.synchronize()
+        outs_b[r * G:(r + 1) * G].copy_(stage)        # eager work between the replays
+    torch.cuda.synchronize()
+    assert torch.equal(outs_a, outs_b)
+    for nm in names:
+        assert torch.equal(getattr(a, nm), getattr(b, nm)), nm
+    assert int(a.slot_pos.max()) == w.steps - 1
+
+
 def test_determinism_bitwise():
     w = WORKLOADS[2]
     announce(f"[determinism] {w.name} twice")
