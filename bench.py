@@ -926,7 +926,7 @@ def main():
         "phase_ms": {"prefill": pre_ms, "decode": dec_ms},
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_resident_kernel<_Float16,128,256> (one launch per decode step)",
+            "kernel": "decode_resident_kernel<_Float16,128,256,false> (one launch per decode step)",
             "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": dec_gbs / HBM_PEAK_GBS, "traffic": decode_traffic(),
             "avg_launch_us": dec_kernel_us, "algorithmic_bytes_per_launch": dec_bytes,
@@ -956,7 +956,7 @@ def main():
     if not args.no_cold:
         result["hbm_measured_ceiling"] = hbm_ceiling()
         result["roofline_cold"] = decode_cold(w)
-        result["roofline_cold"]["kernel"] = "decode_resident_kernel<_Float16,128,256>, MALL-cold"
+        result["roofline_cold"]["kernel"] = "decode_resident_kernel<_Float16,128,256,false>, MALL-cold"
         if not args.no_decode_shapes:
             result["decode_cold_by_workload"] = decode_cold_by_workload()
     if not args.no_dense:
