@@ -186,3 +186,61 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(abi, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(RuntimeError, match="not built"):
         abi.library()
+
+
+C_PROGRAM = r"""
+#include <stdio.h>
+#include <string.h>
+#include "h2o.h"
+
+int main(void) {
+  /* Fake device addresses: only host-side checks run, nothing is dereferenced. */
+  static char slots[64];
+  h2o_cache_desc d;
+  memset(&d, 0, sizeof d);
+  d.batch = 8; d.heads = 32; d.head_dim = 128; d.k_heavy = 52; d.k_local = 52;
+  d.dtype = H2O_F16; d.k_slots = slots; d.v_slots = slots + 16;
+  d.slot_pos = (int32_t*)(void*)(slots + 32); d.acc_score = (float*)(void*)(slots + 48);
+  d.policy = H2O_POLICY_H2O; d.slot_format = H2O_SLOTS_INPUT; d.k_scale = 1.0f; d.v_scale = 1.0f;
+  printf("ws %zu\n", h2o_workspace_bytes(&d, 512));
+  {
+    h2o_status st = h2o_decode_step(&d, 512, NULL, slots, slots, (float*)(void*)slots, NULL,
+                                    NULL, 0, NULL);
+    printf("st %d %s\n", (int)st, h2o_status_str(st));
+    printf("err %s\n", h2o_last_error());
+  }
+  d.k_local = 0;
+  printf("desc %d\n", (int)h2o_reset(&d, NULL));
+  return 0;
+}
+"""
+
+
+def test_header_is_c99_and_links_from_c(tmp_path):
+    # include/h2o.h is a plain C header: a C99 program compiles against it with warnings as
+    # errors, links libh2o.so, and sees the same host-side results as the Python binding.
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "abi_check.c"
+    src.write_text(C_PROGRAM)
+    exe = tmp_path / "abi_check"
+    from kv_cache_eviction_03_amd._abi import LIB_PATH
+    lib_dir = os.path.dirname(LIB_PATH)
+    cmd = [cc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+           f"-I{os.path.join(ROOT, 'include')}",
+           str(src), "-o", str(exe), f"-L{lib_dir}", "-lh2o", f"-Wl,-rpath,{lib_dir}",
+           "-L/opt/rocm/lib", "-Wl,-rpath,/opt/rocm/lib"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stderr
+    lines = dict(line.split(" ", 1) for line in r.stdout.strip().splitlines())
+    assert int(lines["ws"]) == h2o.h2o_workspace_bytes(
+        desc(batch=8, heads=32, k_heavy=52, k_local=52), 512) > 0
+    st, name = lines["st"].split(" ", 1)
+    assert int(st) == h2o.H2O_ERR_INVALID and name == h2o.h2o_status_str(h2o.H2O_ERR_INVALID)
+    assert "NULL" in lines["err"]
+    assert int(lines["desc"]) == h2o.H2O_ERR_INVALID
