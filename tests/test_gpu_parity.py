@@ -66,8 +66,10 @@ SMALL = [
     Workload(97, "tiles-bf16", 1, 1, 4, 128, "bf16", 128, 16, 20, 12, heavy_frac=0.05, sinks=4),
     # fp32 d=128 with k = 300: the split decode (five 64-slot chunks, then the combine)
     Workload(88, "split-f32-d128", 1, 1, 2, 128, "f32", 280, 40, 150, 150),
-    # bf16 d=64 with k = 1500: six 256-slot chunks; 1024-thread combine loops over slots
+    # bf16 d=64 with k = 1500: six 256-slot chunks, then the 512-thread combine
     Workload(89, "split-bf16-d64", 1, 1, 2, 64, "bf16", 1400, 150, 750, 750, heavy_frac=0.05),
+    # heavy hitters only (k_local = 1: the window holds just the new token), fp16 d=128
+    Workload(68, "heavy-only-f16", 2, 1, 2, 128, "f16", 90, 30, 20, 1, heavy_frac=0.05),
     # k = 8192 (the maximum), fp32 d=128: 129 split workgroups per unit (the combine's
     # partial-out loop past its first 64 splits) and 8192 slots (its score loop past 4096)
     Workload(86, "maxk-f32-d128", 1, 1, 1, 128, "f32", 8400, 4, 8000, 192),
