@@ -191,20 +191,23 @@ __device__ __forceinline__ uint64_t score_key(float a, int pos) {
 
 // ------------------------------------------------------------------ resident --
 
-template <typename T, int D, int THREADS, bool F8>
+template <typename T, int D, int THREADS, bool F8, int UB = kBatch>
+// UB slots per row group (kBatch, or 7 for the 1024-thread E4M3 shape when k + 1 <= 448).
 // Register budget: at most 128 VGPRs for the 256-thread shape, so that at least four
 // workgroups share a CU (three per CU measured 3.5% slower on the 32-layer LLaMA-7B-shaped
 // stack). The kernels currently need about 92. The 1024-thread E4M3 shape is held to 64
-// (eight waves per SIMD, two workgroups per CU; about four VGPRs spill): 29.1 -> 27.2 us on
-// the OPT-30B layer. The same cap on the 256-thread E4M3 shape measured slower (12.5 ->
-// 15.8 us on the LLaMA-7B layer), and the fp16 / bf16 shapes need about 92.
+// (eight waves per SIMD, two workgroups per CU). With seven slots per row group it fits
+// without spilling (OPT-30B layer 29.1 us uncapped, 27.2 us capped with eight slots and
+// four spilled VGPRs, 20.7 us capped with seven). The same cap on the 256-thread E4M3 shape
+// measured slower (12.5 -> 15.8 us on the LLaMA-7B layer), and the fp16 / bf16 shapes need
+// about 92 (at 64 they spill over twenty).
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(
     THREADS == 256 ? 4 : (F8 ? 8 : 1), 8)))
 void decode_resident_kernel(DecodeParams p) {
   using S = Shape<T, D, THREADS>;
   using SC = SlotChunk<T, F8>;
   using SE = typename SC::elem;
-  constexpr int VEC = S::VEC, LANES = S::LANES, ROWS = S::ROWS, U = kBatch;
+  constexpr int VEC = S::VEC, LANES = S::LANES, ROWS = S::ROWS, U = UB;
   static_assert(U <= LANES, "a lane owns one slot score");
   __shared__ __attribute__((aligned(16))) float s_red[ROWS * D];
   __shared__ float s_m[ROWS], s_l[ROWS];
@@ -589,8 +592,15 @@ hipError_t run(const DecodeParams& p, const SplitScratch& w, hipStream_t s) {
   if (plan.splits == 0) {
     if (plan.threads == 256)
       decode_resident_kernel<T, D, 256, F8><<<dim3(p.units), dim3(256), 0, s>>>(p);
-    else
+    else {
+      if constexpr (F8) {
+        if (p.k + 1 <= Shape<T, D, 1024>::ROWS * 7) {
+          decode_resident_kernel<T, D, 1024, F8, 7><<<dim3(p.units), dim3(1024), 0, s>>>(p);
+          return hipGetLastError();
+        }
+      }
       decode_resident_kernel<T, D, 1024, F8><<<dim3(p.units), dim3(1024), 0, s>>>(p);
+    }
     return hipGetLastError();
   }
   decode_split_partial_kernel<T, D, F8>

@@ -463,9 +463,13 @@ E4M3_CASES = [
              k_scale=0.5, v_scale=0.25),
     Workload(74, "e4m3-f16-empty-prompt", 1, 1, 3, 64, "f16", 0, 40, 12, 12,
              slot_format="e4m3"),
-    # the 1024-thread resident decode (k = 300) and the split decode (k = 600), with Top-K
+    # the 1024-thread resident decode with seven slots per row group (k = 300), and the
+    # split decode (k = 600), with Top-K
     Workload(73, "e4m3-f16-k300", 1, 1, 2, 128, "f16", 360, 30, 150, 150, heavy_frac=0.05,
              slot_format="e4m3", k_scale=0.75, v_scale=0.6),
+    # the 1024-thread resident decode with eight slots per row group (k + 1 > 448)
+    Workload(67, "e4m3-f16-k480", 1, 1, 2, 128, "f16", 540, 30, 240, 240, heavy_frac=0.05,
+             slot_format="e4m3"),
     Workload(72, "e4m3-bf16-split", 1, 1, 2, 128, "bf16", 700, 30, 300, 300, heavy_frac=0.05,
              slot_format="e4m3", k_scale=1.3),
     Workload(71, "e4m3-f16-split-topk", 1, 1, 2, 128, "f16", 650, 24, 320, 280,
