@@ -192,17 +192,20 @@ __device__ __forceinline__ uint64_t score_key(float a, int pos) {
 // ------------------------------------------------------------------ resident --
 
 template <typename T, int D, int THREADS, bool F8, int UB = kBatch>
-// UB slots per row group (kBatch, or 7 for the 1024-thread E4M3 shape when k + 1 <= 448).
+// UB slots per row group: kBatch, or 7 for 16-bit inputs when k + 1 <= 7 row groups' worth
+// (the k = 104 caches of the OPT-6.7B and LLaMA-7B layers need 105 of the 112 slots; the
+// OPT-30B layer's 411 need 7 of 8 at 1024 threads): one load and one logit fewer per lane.
 // Register budget: at most 128 VGPRs for the 256-thread shape, so that at least four
 // workgroups share a CU (three per CU measured 3.5% slower on the 32-layer LLaMA-7B-shaped
-// stack). The kernels currently need about 92. The 1024-thread E4M3 shape is held to 64
-// (eight waves per SIMD, two workgroups per CU). With seven slots per row group it fits
-// without spilling (OPT-30B layer 29.1 us uncapped, 27.2 us capped with eight slots and
-// four spilled VGPRs, 20.7 us capped with seven). The same cap on the 256-thread E4M3 shape
-// measured slower (12.5 -> 15.8 us on the LLaMA-7B layer), and the fp16 / bf16 shapes need
-// about 92 (at 64 they spill over twenty).
+// stack); fp16 / bf16 need about 92 with eight slots and 85 with seven (at 64 they spill).
+// The E4M3 shapes with seven slots are held to 64 VGPRs (eight waves per SIMD) and fit
+// without spilling: the 256-thread one then runs eight workgroups per CU (the LLaMA-7B
+// layer's 2048 all at once; 12.7 -> 12.3 us), the 1024-thread one two per CU (OPT-30B layer
+// 29.1 us uncapped, 27.2 us capped with eight slots and four spilled VGPRs, 20.7 us capped
+// with seven). The cap with eight slots spilled and measured slower on the 256-thread
+// shape (12.5 -> 15.8 us on the LLaMA-7B layer).
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(
-    THREADS == 256 ? 4 : (F8 ? 8 : 1), 8)))
+    THREADS == 256 ? (UB == 7 && F8 ? 8 : 4) : (F8 ? 8 : 1), 8)))
 void decode_resident_kernel(DecodeParams p) {
   using S = Shape<T, D, THREADS>;
   using SC = SlotChunk<T, F8>;
@@ -590,8 +593,15 @@ template <typename T, int D, bool F8 = false>
 hipError_t run(const DecodeParams& p, const SplitScratch& w, hipStream_t s) {
   const DecodePlan plan = plan_decode(sizeof(T), D, p.k, p.units);
   if (plan.splits == 0) {
-    if (plan.threads == 256)
+    if (plan.threads == 256) {
+      if constexpr (sizeof(T) == 2) {
+        if (p.k + 1 <= Shape<T, D, 256>::ROWS * 7) {
+          decode_resident_kernel<T, D, 256, F8, 7><<<dim3(p.units), dim3(256), 0, s>>>(p);
+          return hipGetLastError();
+        }
+      }
       decode_resident_kernel<T, D, 256, F8><<<dim3(p.units), dim3(256), 0, s>>>(p);
+    }
     else {
       if constexpr (F8) {
         if (p.k + 1 <= Shape<T, D, 1024>::ROWS * 7) {

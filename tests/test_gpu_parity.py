@@ -68,6 +68,10 @@ SMALL = [
     Workload(88, "split-f32-d128", 1, 1, 2, 128, "f32", 280, 40, 150, 150),
     # bf16 d=64 with k = 1500: six 256-slot chunks, then the 512-thread combine
     Workload(89, "split-bf16-d64", 1, 1, 2, 64, "bf16", 1400, 150, 750, 750, heavy_frac=0.05),
+    # 256-thread resident decode with eight slots per row group (k + 1 above the 112 or 224
+    # slots that seven cover at d = 128 or d = 64)
+    Workload(66, "eight-slots-f16-d128", 2, 1, 2, 128, "f16", 180, 30, 60, 60, heavy_frac=0.05),
+    Workload(65, "eight-slots-bf16-d64", 1, 1, 2, 64, "bf16", 300, 30, 120, 120, heavy_frac=0.05),
     # heavy hitters only (k_local = 1: the window holds just the new token), fp16 d=128
     Workload(68, "heavy-only-f16", 2, 1, 2, 128, "f16", 90, 30, 20, 1, heavy_frac=0.05),
     # k = 8192 (the maximum), fp32 d=128: 129 split workgroups per unit (the combine's
@@ -467,6 +471,9 @@ E4M3_CASES = [
     # split decode (k = 600), with Top-K
     Workload(73, "e4m3-f16-k300", 1, 1, 2, 128, "f16", 360, 30, 150, 150, heavy_frac=0.05,
              slot_format="e4m3", k_scale=0.75, v_scale=0.6),
+    # the 256-thread resident decode with eight slots per row group (k + 1 > 112)
+    Workload(64, "e4m3-f16-k120", 2, 1, 2, 128, "f16", 180, 30, 60, 60, heavy_frac=0.05,
+             slot_format="e4m3"),
     # the 1024-thread resident decode with eight slots per row group (k + 1 > 448)
     Workload(67, "e4m3-f16-k480", 1, 1, 2, 128, "f16", 540, 30, 240, 240, heavy_frac=0.05,
              slot_format="e4m3"),
