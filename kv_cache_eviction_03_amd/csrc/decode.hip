@@ -197,7 +197,8 @@ template <typename T, int D, int THREADS, bool F8, int UB = kBatch>
 // OPT-30B layer's 411 need 7 of 8 at 1024 threads): one load and one logit fewer per lane.
 // Register budget: at most 128 VGPRs for the 256-thread shape, so that at least four
 // workgroups share a CU (three per CU measured 3.5% slower on the 32-layer LLaMA-7B-shaped
-// stack); fp16 / bf16 need about 92 with eight slots and 85 with seven (at 64 they spill).
+// stack); fp16 / bf16 need about 92 with eight slots and 85 with seven (at 64 they spill);
+// the 1024-thread fp16 shape with seven ran the OPT-30B layer in 38.5 us against 38.9.
 // The E4M3 shapes with seven slots are held to 64 VGPRs (eight waves per SIMD) and fit
 // without spilling: the 256-thread one then runs eight workgroups per CU (the LLaMA-7B
 // layer's 2048 all at once; 12.7 -> 12.3 us), the 1024-thread one two per CU (OPT-30B layer
@@ -603,7 +604,7 @@ hipError_t run(const DecodeParams& p, const SplitScratch& w, hipStream_t s) {
       decode_resident_kernel<T, D, 256, F8><<<dim3(p.units), dim3(256), 0, s>>>(p);
     }
     else {
-      if constexpr (F8) {
+      if constexpr (sizeof(T) == 2) {
         if (p.k + 1 <= Shape<T, D, 1024>::ROWS * 7) {
           decode_resident_kernel<T, D, 1024, F8, 7><<<dim3(p.units), dim3(1024), 0, s>>>(p);
           return hipGetLastError();
