@@ -72,6 +72,8 @@ SMALL = [
     # slots that seven cover at d = 128 or d = 64)
     Workload(66, "eight-slots-f16-d128", 2, 1, 2, 128, "f16", 180, 30, 60, 60, heavy_frac=0.05),
     Workload(65, "eight-slots-bf16-d64", 1, 1, 2, 64, "bf16", 300, 30, 120, 120, heavy_frac=0.05),
+    # 1024-thread resident decode with eight slots per row group (k + 1 > 448), fp16
+    Workload(63, "eight-slots-f16-k480", 1, 1, 2, 128, "f16", 540, 30, 240, 240, heavy_frac=0.05),
     # heavy hitters only (k_local = 1: the window holds just the new token), fp16 d=128
     Workload(68, "heavy-only-f16", 2, 1, 2, 128, "f16", 90, 30, 20, 1, heavy_frac=0.05),
     # k = 8192 (the maximum), fp32 d=128: 129 split workgroups per unit (the combine's
