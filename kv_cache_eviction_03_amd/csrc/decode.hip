@@ -45,6 +45,9 @@ namespace h2o {
 namespace {
 
 constexpr int kBatch = 8;         // slot rows per row group in one load batch
+// The split partial kernel's: 7 makes 37 chunks of 112 slots for the 4096-slot stream
+// instead of 33 of 128 (the last holding one slot), 17.4 -> 17.1 us per step.
+constexpr int kPartBatch = 7;
 
 template <typename T, int D, int THREADS = 256> struct Shape {
   static constexpr int VEC = Chunk<T>::N;       // elements per 16-byte chunk
@@ -359,7 +362,7 @@ __global__ __launch_bounds__(kPartThreads) void decode_split_partial_kernel(Deco
   using S = Shape<T, D, kPartThreads>;
   using SC = SlotChunk<T, F8>;
   using SE = typename SC::elem;
-  constexpr int VEC = S::VEC, LANES = S::LANES, ROWS = S::ROWS, U = kBatch;
+  constexpr int VEC = S::VEC, LANES = S::LANES, ROWS = S::ROWS, U = kPartBatch;
   constexpr int C = ROWS * U;                   // slots per workgroup
   __shared__ __attribute__((aligned(16))) float s_red[ROWS * D];
   __shared__ float s_m[ROWS], s_l[ROWS], s_sc[ROWS];
@@ -629,7 +632,7 @@ DecodePlan plan_decode(int elem_bytes, int D, int k, int units) {
   DecodePlan plan{256, 0};
   if (k + 1 <= (256 / lanes) * kBatch) return plan;
   if (k + 1 <= (1024 / lanes) * kBatch) { plan.threads = 1024; return plan; }
-  const int chunk = (kPartThreads / lanes) * kBatch;
+  const int chunk = (kPartThreads / lanes) * kPartBatch;
   plan.splits = (k + 1 + chunk - 1) / chunk;
   return plan;
 }

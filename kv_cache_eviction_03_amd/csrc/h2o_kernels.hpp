@@ -155,7 +155,7 @@ struct DecodePlan {
   int splits;
 };
 DecodePlan plan_decode(int elem_bytes, int D, int k, int units);
-constexpr int kMaxSplits = 160;   // enough for k <= 8192 at 64 slots per split
+constexpr int kMaxSplits = 160;   // enough for k <= 8192 at 56 slots per split (147)
 
 // Workspace of the split decode: per-split partials plus the step's logits.
 struct SplitScratch {

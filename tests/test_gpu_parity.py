@@ -64,9 +64,9 @@ SMALL = [
     Workload(96, "t1-f32-d64", 1, 1, 1, 64, "f32", 1, 6, 1, 1),
     # prompt of exactly two tiles, bf16 d=128, several heavy hitters
     Workload(97, "tiles-bf16", 1, 1, 4, 128, "bf16", 128, 16, 20, 12, heavy_frac=0.05, sinks=4),
-    # fp32 d=128 with k = 300: the split decode (five 64-slot chunks, then the combine)
+    # fp32 d=128 with k = 300: the split decode (six 56-slot chunks, then the combine)
     Workload(88, "split-f32-d128", 1, 1, 2, 128, "f32", 280, 40, 150, 150),
-    # bf16 d=64 with k = 1500: six 256-slot chunks, then the 512-thread combine
+    # bf16 d=64 with k = 1500: seven 224-slot chunks, then the 512-thread combine
     Workload(89, "split-bf16-d64", 1, 1, 2, 64, "bf16", 1400, 150, 750, 750, heavy_frac=0.05),
     # 256-thread resident decode with eight slots per row group (k + 1 above the 112 or 224
     # slots that seven cover at d = 128 or d = 64)
@@ -76,7 +76,7 @@ SMALL = [
     Workload(63, "eight-slots-f16-k480", 1, 1, 2, 128, "f16", 540, 30, 240, 240, heavy_frac=0.05),
     # heavy hitters only (k_local = 1: the window holds just the new token), fp16 d=128
     Workload(68, "heavy-only-f16", 2, 1, 2, 128, "f16", 90, 30, 20, 1, heavy_frac=0.05),
-    # k = 8192 (the maximum), fp32 d=128: 129 split workgroups per unit (the combine's
+    # k = 8192 (the maximum), fp32 d=128: 147 split workgroups per unit (the combine's
     # partial-out loop past its first 64 splits) and 8192 slots (its score loop past 4096)
     Workload(86, "maxk-f32-d128", 1, 1, 1, 128, "f32", 8400, 4, 8000, 192),
     # T + k = 15900 words: the seed keeps the column sums in global memory, not LDS
