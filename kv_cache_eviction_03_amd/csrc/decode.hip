@@ -38,6 +38,7 @@
 // The victim is chosen with 64-bit keys (fp32 score bits << 32 | position):
 // scores are >= 0, so the integer order is the (score, position) order.
 // All reductions run in a fixed order: results are bit-reproducible.
+#include "../../include/h2o.h"
 #include "h2o_device.hpp"
 #include "h2o_kernels.hpp"
 
@@ -352,6 +353,11 @@ void decode_resident_kernel(DecodeParams p) {
 // --------------------------------------------------------------------- split --
 
 constexpr int kPartThreads = 256;
+// The largest cache (H2O_MAX_SLOTS, fp32 at d = 128: 32 lanes per row, the smallest chunk)
+// must split into no more chunks than the combine's tables hold.
+constexpr int kMinChunk = (kPartThreads / 32) * kPartBatch;
+static_assert((H2O_MAX_SLOTS + kMinChunk) / kMinChunk <= kMaxSplits,
+              "split count of the largest cache exceeds kMaxSplits");
 // 512 threads with 8 slots each per load batch: 1024 threads with 4 measured 5% slower on
 // the 4096-slot stream (fewer waves to launch on the unit's CU, the same one round trip).
 constexpr int kCombThreads = 512;

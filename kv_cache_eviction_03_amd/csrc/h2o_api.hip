@@ -229,6 +229,9 @@ h2o_status decode_impl(const h2o_cache_desc* c, int64_t t, const int32_t* tpos, 
 
   const h2o::DecodePlan plan =
       h2o::plan_decode((int)elem_bytes(c->dtype), c->head_dim, slots_of(c), units_of(c));
+  if (plan.splits > h2o::kMaxSplits)
+    return fail(H2O_ERR_UNSUPPORTED, "k = %d needs %d decode splits, more than %d",
+                slots_of(c), plan.splits, h2o::kMaxSplits);
   if ((int64_t)units_of(c) * (plan.splits ? plan.splits : 1) > 0x7fffffffLL)
     return fail(H2O_ERR_UNSUPPORTED, "batch * heads * %d decode workgroups exceed the grid limit",
                 plan.splits);
