@@ -13,7 +13,7 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests need a device; off the GPU machine they are skipped rather than failed.
+    # GPU tests need a device; on a machine without one they are skipped rather than failed.
     try:
         import torch
         have_gpu = torch.cuda.is_available()
