@@ -1,0 +1,86 @@
+"""GPU parity over a seeded sweep of small random configurations.
+
+The fixed cases elsewhere each aim at one code path; this sweep draws shapes,
+budgets, dtypes, policies and slot formats together from one seeded generator,
+so that combinations nobody wrote down by hand (a prompt that ends one row into
+a tile, a budget split with k_heavy = 0, a sinks count above k_heavy, E4M3 slots
+on a cache that only ever appends, a split decode under a position policy) meet
+the oracle too. Every unit of every
+configuration is compared, prefill outputs, column sums, slots and every decode
+step, with the same tolerances as the fixed cases.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from tests.parity import check_units, run_gpu
+from workloads import Workload, generate
+
+N_CONFIGS = 64
+
+
+def sweep_configs(n=N_CONFIGS, seed=2026):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dtype = str(rng.choice(["f16", "bf16", "f32"], p=[0.4, 0.4, 0.2]))
+        d = int(rng.choice([64, 128]))
+        k_local = int(rng.integers(1, 65))
+        k_heavy = int(rng.choice([0, int(rng.integers(1, 33)), int(rng.integers(33, 321)),
+                                  int(rng.integers(321, 1001))], p=[0.15, 0.4, 0.33, 0.12]))
+        k = k_heavy + k_local
+        shape = rng.random()
+        if shape < 0.1:
+            T = 0                                   # empty prompt: the decode fills the cache
+        elif shape < 0.3:
+            T = int(rng.integers(1, k + 1))         # every prompt position kept
+        else:
+            T = int(rng.integers(k + 1, k + 701))   # the seed selects
+        policy = str(rng.choice(["h2o", "sinks", "strided", "topk"], p=[0.55, 0.15, 0.15, 0.15]))
+        param = {"h2o": 0, "topk": 0, "sinks": int(rng.integers(0, 9)),
+                 "strided": int(rng.integers(1, 17))}[policy]
+        e4m3 = dtype != "f32" and rng.random() < 0.25
+        kw = dict(heavy_frac=float(rng.choice([0.0, 0.05])), sinks=int(rng.choice([0, 4])),
+                  policy=policy, policy_param=param)
+        if e4m3:
+            kw.update(slot_format="e4m3", k_scale=float(rng.uniform(0.2, 2.0)),
+                      v_scale=float(rng.uniform(0.2, 2.0)))
+        out.append(Workload(20 + i, f"sweep{i:02d}", int(rng.integers(1, 3)), 1,
+                            int(rng.integers(1, 4)), d, dtype, T, int(rng.integers(1, 61)),
+                            k_heavy, k_local, **kw))
+    return out
+
+
+CONFIGS = sweep_configs()
+
+
+def test_sweep_is_fixed_and_valid():
+    """The sweep is a pure function of its seed and stays inside the library's limits."""
+    again = sweep_configs()
+    assert again == CONFIGS
+    for w in CONFIGS:
+        assert w.k_local >= 1 and 1 <= w.k <= 8192
+        assert w.slot_format == "input" or w.dtype != "f32"
+    # the draw reaches the paths it is meant to mix
+    assert any(w.prompt == 0 for w in CONFIGS)
+    assert any(0 < w.prompt <= w.k for w in CONFIGS)
+    assert any(w.k_heavy == 0 for w in CONFIGS)
+    assert any(w.slot_format == "e4m3" for w in CONFIGS)
+    assert {w.policy for w in CONFIGS} == {"h2o", "sinks", "strided", "topk"}
+    # caches past one workgroup's reach at d = 128 (split decode)
+    assert any(w.k + 1 > 511 and w.head_dim == 128 for w in CONFIGS)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("w", CONFIGS, ids=[w.name for w in CONFIGS])
+def test_random_configuration_every_unit(w):
+    print(f"[sweep] {w.name}: B={w.batch} H={w.heads} d={w.head_dim} {w.dtype} T={w.prompt} "
+          f"n={w.steps} k={w.k_heavy}+{w.k_local} {w.policy}({w.policy_param}) "
+          f"{w.slot_format} heavy_frac={w.heavy_frac} sinks={w.sinks}", flush=True)
+    sys.stdout.flush()
+    x = generate(w, seed=0, device="cuda")
+    r = run_gpu(w, x)
+    agg = check_units(w, x, r, range(w.units_per_layer))
+    print(f"[sweep] {w.name}: prefill {agg['prefill_out']:.2e} decode {agg['decode_out']:.2e} "
+          f"ties={len(agg['ties'])}", flush=True)
