@@ -65,11 +65,15 @@ candidates (pos <= t - k_local), the minimum of (key, position):
   "strided"  seed score [j % s == 0], key = [pos % s == 0]: the window plus the
              most recent multiples of the stride s;
   "topk"     key = this step's probability p of the slot (the token with the
-             least attention now goes); its seeding uses c_j (R13).
+             least attention now goes); seed score = the prompt's last row of
+             attention, P[T-1, j] (R13).
 Local is "h2o" with k_heavy = 0, heavy-only is k_local = 1. The running score acc
 is kept under every policy.
-  R13 The pages give Top-K no prompt-time score; the column sum (the same
-      cumulative attention H2O seeds with) is used.
+  R13 [blog] §3.1.1 defines Top-K as keeping the tokens with the highest current
+      attention score. At a decode step the current attention is that step's
+      softmax row; at the end of the prompt it is the last prompt row, P[T-1, :],
+      so Top-K seeds by fl32(P[T-1, j]). (The running score acc still starts
+      from the column sums under every policy.)
 
 Quantised slots. [blog] §3.3 Q3 reports that H2O combines with KV quantisation
 but names no scheme. With slot_format "e4m3" every K/V row that enters a slot
@@ -180,11 +184,17 @@ def quantize_row(x, scale):
     return e4m3_encode(r), r * float(s32)
 
 
-def policy_seed_scores(policy: str, param: int, c32: np.ndarray) -> np.ndarray:
-    """The fp32 score each prompt position is ranked by at seeding (see the header)."""
+def policy_seed_scores(policy: str, param: int, c32: np.ndarray,
+                       last_row: np.ndarray | None = None) -> np.ndarray:
+    """The fp32 score each prompt position is ranked by at seeding (see the header).
+
+    c32: the fp32 column sums; last_row: the prompt's last attention row P[T-1, :]
+    in float64 (used by "topk", R13)."""
     j = np.arange(len(c32))
-    if policy in ("h2o", "topk"):
+    if policy == "h2o":
         return np.asarray(c32, dtype=np.float32)
+    if policy == "topk":
+        return np.asarray(last_row, dtype=np.float64).astype(np.float32)
     if policy == "sinks":
         return (j < param).astype(np.float32)
     if policy == "strided":
@@ -291,13 +301,44 @@ def _near(a: float, b: float, rel_tol: float) -> bool:
     return abs(a - b) <= rel_tol * max(abs(a), abs(b))
 
 
+def adopt_prefill_kept(kept, other, score, T, k_local, rel_tol=1e-5):
+    """Whether another implementation's kept set `other` may replace the oracle's `kept`.
+
+    The rule (near ties at the heavy cutoff, R10 + the tolerance rule of the header):
+    `other` must be a set of distinct prompt positions in [0, T) of the oracle's size
+    that holds the whole recent window, and every position it keeps instead of the
+    oracle's must score within rel_tol (relative, on the fp32 seed scores) of every
+    position the oracle keeps instead of it. Returns (theirs, ours) — the positions
+    kept only by `other` and only by the oracle — or raises ParityError.
+    """
+    other = [int(p) for p in other]
+    theirs = sorted(set(other) - set(kept))
+    ours = sorted(set(kept) - set(other))
+    why = None
+    if len(set(other)) != len(other):
+        why = "a position is kept twice"
+    elif len(other) != len(kept):
+        why = f"{len(other)} positions kept instead of {len(kept)}"
+    elif any(not 0 <= p < T for p in other):
+        why = "a kept position lies outside the prompt"
+    elif set(range(max(0, T - k_local), T)) - set(other):
+        why = "a recent-window position is missing"
+    elif not (len(theirs) == len(ours) > 0):
+        why = "the sets differ in size"
+    elif not all(_near(float(score[x]), float(score[y]), rel_tol) for x in theirs for y in ours):
+        why = "the swapped scores are not within the tolerance"
+    if why is not None:
+        raise ParityError(f"prefill kept sets differ beyond a near tie ({why}): "
+                          f"only theirs {theirs}, only ours {ours}")
+    return theirs, ours
+
+
 def prefill(cache: UnitCache, Q, K, V, adopt_kept=None, rel_tol=1e-5):
     """Run the prompt through one unit and seed its cache.
 
     Returns (O, c64): O = P V (float64, [T, d]) and the float64 column sums.
-    `adopt_kept`, if given, is another implementation's kept position set; it
-    is adopted when every position it keeps instead of the oracle's is a near
-    tie (rel_tol on the fp32 scores) with one the oracle keeps instead of it.
+    `adopt_kept`, if given, is another implementation's kept positions (a list);
+    it is adopted when adopt_prefill_kept accepts it, and the swap is logged.
     """
     Q, K, V = (np.asarray(x, dtype=np.float64) for x in (Q, K, V))
     T = Q.shape[0]
@@ -307,24 +348,15 @@ def prefill(cache: UnitCache, Q, K, V, adopt_kept=None, rel_tol=1e-5):
     O = P @ V
     c64 = column_sums(P)
     c32 = c64.astype(np.float32)
-    score = policy_seed_scores(cache.policy, cache.policy_param, c32)
+    score = policy_seed_scores(cache.policy, cache.policy_param, c32, last_row=P[T - 1])
     kept = seed_positions(score, cache.k_heavy, cache.k_local)
 
     if adopt_kept is not None:
-        other = sorted(int(p) for p in adopt_kept)
-        if other != kept:
-            theirs = set(other) - set(kept)
-            ours = set(kept) - set(other)
-            local = set(range(max(0, T - cache.k_local), T))
-            ok = (len(other) == len(kept) and not (local - set(other))
-                  and all(0 <= p < T for p in other)
-                  and all(_near(float(score[x]), float(score[y]), rel_tol)
-                          for x in theirs for y in ours))
-            if not ok:
-                raise ParityError(f"prefill kept sets differ beyond a near tie: "
-                                  f"only theirs {sorted(theirs)}, only ours {sorted(ours)}")
-            cache.ties.append(("prefill", T, sorted(theirs), sorted(ours)))
-            kept = other
+        other = [int(p) for p in adopt_kept]
+        if sorted(other) != kept:
+            theirs, ours = adopt_prefill_kept(kept, other, score, T, cache.k_local, rel_tol)
+            cache.ties.append(("prefill", T, theirs, ours))
+            kept = sorted(other)
 
     for j in range(T):
         cache.hist32[j] = c32[j]

@@ -16,7 +16,8 @@ import pytest
 import torch
 from hypothesis import given, settings, strategies as st
 
-from oracle import UnitCache, ParityError, decode, prefill, run_unit, seed_positions
+from oracle import (UnitCache, ParityError, adopt_prefill_kept, decode, prefill, run_unit,
+                    seed_positions)
 from tests.bruteforce import replay
 
 
@@ -276,6 +277,65 @@ def test_near_tie_adoption_accepts_ties_and_rejects_the_rest():
         decode(fresh(), 7, np.ones(d), np.full(d, 0.25), np.ones(d), adopt_victim=3)
 
 
+# Prefill near-tie adoption: another implementation's kept set replaces the oracle's only
+# when it is a set of the same size that holds the window and differs by swaps whose fp32
+# scores lie within the tolerance (the tolerance rule applied at the heavy cutoff).
+
+def _cutoff_scores():
+    # Candidates 0..7 (T = 10, k_local = 2), k_heavy = 3. The oracle keeps 5, 6, 1 (scores
+    # 9, 8, 7); position 3 is 1e-6 relative below 1 (a near tie), position 4 is 1e-4 below.
+    s = np.array([1.0, 7.0, 0.5, 7.0 * (1 - 1e-6), 7.0 * (1 - 1e-4), 9.0, 8.0, 0.25, 0.1, 0.1],
+                 dtype=np.float32)
+    kept = seed_positions(s, 3, 2)
+    assert kept == [1, 5, 6, 8, 9]
+    return s, kept
+
+
+def test_prefill_adoption_accepts_a_near_tie_swap():
+    s, kept = _cutoff_scores()
+    theirs, ours = adopt_prefill_kept(kept, [3, 5, 6, 8, 9], s, 10, 2)
+    assert theirs == [3] and ours == [1]
+
+
+@pytest.mark.parametrize("other,why", [
+    ([4, 5, 6, 8, 9], "not within the tolerance"),      # swap at 1e-4 relative
+    ([0, 5, 6, 8, 9], "not within the tolerance"),      # a low score
+    ([5, 5, 6, 8, 9], "kept twice"),                    # a duplicated position
+    ([1, 1, 5, 6, 8, 9], "kept twice"),
+    ([1, 3, 5, 6, 8, 9], "instead of 5"),               # one too many
+    ([5, 6, 8, 9], "instead of 5"),                     # one too few
+    ([1, 3, 5, 6, 9], "recent-window position is missing"),
+    ([1, 5, 6, 9, 10], "outside the prompt"),           # position T
+    ([-1, 5, 6, 8, 9], "outside the prompt"),
+])
+def test_prefill_adoption_rejects_the_rest(other, why):
+    s, kept = _cutoff_scores()
+    with pytest.raises(ParityError, match=why):
+        adopt_prefill_kept(kept, other, s, 10, 2)
+
+
+def test_prefill_adoption_through_the_prompt():
+    # Top-K with Q = 0: the last prompt row is uniform, so every candidate ties exactly and
+    # any swap among candidates is a tie; malformed sets are still refused.
+    T, d, kh, kl = 12, 4, 3, 2
+    rng = np.random.default_rng(3)
+    Q, K, V = np.zeros((T, d)), rng.standard_normal((T, d)), rng.standard_normal((T, d))
+    ref = UnitCache(kh, kl, d, policy="topk")
+    prefill(ref, Q, K, V)
+    assert ref.kept_positions() == [7, 8, 9, 10, 11] and not ref.ties
+    c = UnitCache(kh, kl, d, policy="topk")
+    prefill(c, Q, K, V, adopt_kept=[0, 1, 2, 10, 11])
+    assert c.kept_positions() == [0, 1, 2, 10, 11]
+    assert c.ties == [("prefill", T, [0, 1, 2], [7, 8, 9])]
+    for bad in ([0, 0, 2, 10, 11], [0, 1, 10, 11], [0, 1, 2, 9, 11], [0, 1, 2, 11, 12]):
+        with pytest.raises(ParityError):
+            prefill(UnitCache(kh, kl, d, policy="topk"), Q, K, V, adopt_kept=bad)
+    # under H2O the same prompt's column sums are strictly decreasing (harmonic tails), so
+    # no swap is a tie
+    with pytest.raises(ParityError):
+        prefill(UnitCache(kh, kl, d), Q, K, V, adopt_kept=[0, 1, 3, 10, 11])
+
+
 # ------------------------------------------------------------ brute force -------
 
 def _oracle_victim_positions(cache):
@@ -400,6 +460,44 @@ def test_topk_policy_evicts_the_least_attended_now():
         cache2.hist32[slot], cache2.hist64[slot] = cache2.acc[slot], float(cache2.acc[slot])
     _, v2 = decode(cache2, 5, q, 2.0 * q, np.zeros(d))
     assert v2 == 0
+
+
+def test_topk_seed_zero_query_keeps_the_newest():
+    # Q = 0: the prompt's last attention row is exactly uniform, so every candidate ties
+    # and the newest k_heavy candidates are kept. (Ranking by the column sums instead would
+    # keep the oldest: c_j = H_T - H_j decreases in j.)
+    T, d, kh, kl = 40, 8, 6, 5
+    rng = np.random.default_rng(0)
+    K, V = rng.standard_normal((T, d)), rng.standard_normal((T, d))
+    c = UnitCache(kh, kl, d, policy="topk")
+    prefill(c, np.zeros((T, d)), K, V)
+    assert c.kept_positions() == list(range(T - kl - kh, T))
+    h = UnitCache(kh, kl, d)
+    prefill(h, np.zeros((T, d)), K, V)
+    assert h.kept_positions() == list(range(kh)) + list(range(T - kl, T))
+    # the running scores still start from the column sums: acc_j = H_T - H_j
+    for s_, p in enumerate(c.pos):
+        exact = sum(Fraction(1, i + 1) for i in range(int(p), T))
+        assert abs(float(c.acc[s_]) - float(exact)) <= 1e-6 * float(exact)
+
+
+def test_topk_seed_follows_the_last_row_not_the_column_sums():
+    # Two key directions: keys at the positions in M point along e0, the others along e1.
+    # Every query but the last points along e1 (so the column sums favour positions outside
+    # M), the last one along e0 with a large norm (so its attention sits on M). Top-K keeps M
+    # (the highest current attention); H2O keeps the highest column sums, outside M.
+    T, d, kh, kl = 30, 4, 4, 3
+    M = [2, 9, 15, 21]
+    e0, e1 = np.eye(d)[0], np.eye(d)[1]
+    K = np.array([e0 if j in M else e1 for j in range(T)], dtype=np.float64)
+    Q = np.array([6.0 * e1] * (T - 1) + [6.0 * e0])
+    V = np.random.default_rng(1).standard_normal((T, d))
+    c = UnitCache(kh, kl, d, policy="topk")
+    prefill(c, Q, K, V)
+    assert c.kept_positions() == sorted(M + list(range(T - kl, T)))
+    h = UnitCache(kh, kl, d)
+    prefill(h, Q, K, V)
+    assert not set(M) & set(h.kept_positions())
 
 
 def test_policy_parameters_are_checked():
