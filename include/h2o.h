@@ -77,8 +77,10 @@ typedef enum { H2O_F32 = 0, H2O_F16 = 1, H2O_BF16 = 2 } h2o_dtype;
  *   H2O_POLICY_STRIDED  seed score and key: 1 for positions that are multiples
  *                       of policy_param, else 0 (blog §3.1.1 "Strided"):
  *                       the window plus the latest multiples; policy_param >= 1
- *   H2O_POLICY_TOPK     seed score: c_j; key: the slot's attention probability
- *                       in this step (blog §3.1.1 "Top-K": the token attended
+ *   H2O_POLICY_TOPK     seed score: the prompt's last attention row,
+ *                       P[T-1][j]; key: the slot's attention probability in
+ *                       this step (blog §3.1.1 "Top-K": the tokens with the
+ *                       highest current attention stay, the token attended
  *                       least now leaves)
  * acc_score accumulates every step under every policy. Local is H2O with
  * k_heavy = 0; heavy-only is k_local = 1.
@@ -179,7 +181,8 @@ h2o_status h2o_reset(const h2o_cache_desc* cache, void* stream);
  * Workspace contract: 256-byte aligned device memory owned by the caller. It is
  * scratch: its contents on entry are ignored and on return are unspecified
  * (prefill keeps per-query-block partial column sums there, about T^2 / 256
- * floats per unit for fp16/bf16, and the column sums when colsum_out is NULL;
+ * floats per unit for fp16/bf16, the column sums when colsum_out is NULL, and
+ * under H2O_POLICY_TOPK the last prompt row's attention, T floats per unit;
  * a decode that spreads a unit's slots over several workgroups keeps
  * per-workgroup partials there). The size grows with max_prompt, so a
  * workspace sized for max_prompt serves every shorter prompt. One workspace

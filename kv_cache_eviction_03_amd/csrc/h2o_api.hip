@@ -90,8 +90,9 @@ int part_rows_of(const h2o_cache_desc* c, int64_t T) {
   return c->dtype == H2O_F32 ? (int)(T > 0 ? T : 1) : h2o::kPrefillPartRows;
 }
 struct PrefillLayout {
-  size_t lse2, colpart, colsum, total;   // byte offsets of the parts, total size
+  size_t lse2, colpart, colsum, rank, total;   // byte offsets of the parts, total size
 };
+// Top-K seeds by the last prompt row's attention, kept in its own [units][T] part.
 PrefillLayout prefill_layout(const h2o_cache_desc* c, int64_t T) {
   const size_t units = (size_t)units_of(c);
   const size_t rows = round_up(units * (size_t)T * sizeof(float), kWsAlign);
@@ -101,7 +102,8 @@ PrefillLayout prefill_layout(const h2o_cache_desc* c, int64_t T) {
   l.lse2 = 0;
   l.colpart = c->dtype == H2O_F32 ? rows : 0;
   l.colsum = l.colpart + part;
-  l.total = l.colsum + rows;
+  l.rank = l.colsum + rows;
+  l.total = l.rank + (c->policy == H2O_POLICY_TOPK ? rows : 0);
   return l;
 }
 size_t prefill_scratch(const h2o_cache_desc* c, int64_t T) { return prefill_layout(c, T).total; }
@@ -201,7 +203,14 @@ h2o_status prefill_impl(const h2o_cache_desc* c, const void* q, const void* k, c
     if ((e = h2o::launch_prefill_attn_mfma(dt, D, pp, s)))
       return hip_fail(e, "prefill attention launch");
   }
-  h2o::SeedParams sp{k, v, colpart, colsum, lens, c->k_slots, c->v_slots, c->slot_pos,
+  float* rank = nullptr;
+  if (c->policy == H2O_POLICY_TOPK) {
+    rank = reinterpret_cast<float*>(ws + lay.rank);
+    h2o::LastRowParams lp{q, k, rank, lens, (int32_t)units, c->heads, T, slots_of(c),
+                          qk_scale(D)};
+    if ((e = h2o::launch_last_row(dt, D, lp, s))) return hip_fail(e, "last-row launch");
+  }
+  h2o::SeedParams sp{k, v, colpart, colsum, rank, lens, c->k_slots, c->v_slots, c->slot_pos,
                      c->acc_score, (int32_t)units, c->heads, T, part_rows_of(c, T), c->k_heavy,
                      c->k_local, c->policy, c->policy_param, inv_of(c, c->k_scale),
                      inv_of(c, c->v_scale)};

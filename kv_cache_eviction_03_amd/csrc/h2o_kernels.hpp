@@ -76,7 +76,9 @@ __host__ __device__ inline float policy_key(int policy, int param, float acc, fl
   if (policy == kPolicySinks) return pos < param ? 1.f : 0.f;
   return pos % param == 0 ? 1.f : 0.f;
 }
-// The seed score of prompt position j (column sum c under H2O and Top-K).
+// The seed score of prompt position j: c is the column sum under H2O and the prompt's last
+// attention row P[T-1][j] under Top-K (the highest current attention); position policies
+// rank by their 0/1 class.
 __host__ __device__ inline float policy_seed(int policy, int param, float c, int j) {
   if (policy == kPolicySinks) return j < param ? 1.f : 0.f;
   if (policy == kPolicyStrided) return j % param == 0 ? 1.f : 0.f;
@@ -125,6 +127,8 @@ struct SeedParams {
   const void* v;
   const float* colpart; // [units][colpart_stride(T, part_rows)]
   float* colsum;        // [units][T]: the summed column sums are written here
+  const float* rank;    // [units][T] seed scores other than the column sums (Top-K: the last
+                        // prompt row's attention), or null
   const int32_t* lens;  // [batch] per-sequence prompt lengths <= T (device), or null: T
   void* k_slots;
   void* v_slots;
@@ -139,6 +143,20 @@ struct SeedParams {
   int32_t policy;       // seeding ranking, h2o_policy
   int32_t policy_param;
   float k_inv, v_inv;   // E4M3 slots: fl32(1 / k_scale), fl32(1 / v_scale)
+};
+
+// The prompt's last attention row, P[T-1][j] for j < T (fp32), per unit: the Top-K seed
+// scores.
+struct LastRowParams {
+  const void* q;        // prompt Q/K [units][T][D]
+  const void* k;
+  float* rank;          // [units][T]
+  const int32_t* lens;  // [batch] per-sequence prompt lengths <= T (device), or null: T
+  int32_t units;
+  int32_t heads;
+  int32_t T;            // rows stored per unit
+  int32_t k_slots;      // k: a unit whose prompt fits (T <= k) needs no ranking
+  float qk_scale;       // log2(e) / sqrt(D)
 };
 
 struct ResetParams {
@@ -177,5 +195,6 @@ hipError_t launch_prefill_attn_mfma(DType dt, int D, const PrefillParams& p, hip
 hipError_t launch_prefill_attn_f32(int D, const PrefillParams& p, hipStream_t s);
 hipError_t launch_prefill_colsum_f32(int D, const PrefillParams& p, hipStream_t s);
 hipError_t launch_seed(DType dt, bool f8, int D, const SeedParams& p, hipStream_t s);
+hipError_t launch_last_row(DType dt, int D, const LastRowParams& p, hipStream_t s);
 
 }  // namespace h2o

@@ -3,11 +3,16 @@
 // seed: per unit, keep the last k_local prompt positions (the recent tokens of
 // the H2O blog, ttsmallhot.github.io, §2.2) plus the k_heavy positions of
 // [0, T - k_local) with the highest fp32 column sum, i.e. the top-k of the
-// cumulative attention ("H2O Heavy-Hitter Oracle 分析", §3.1) — or, under a
-// position policy (blog §3.1.1, §3.3 Q1), the highest 0/1 position class. Ties rank the
-// newer position higher, so the older one is dropped. If T <= k every
-// position is kept. Kept positions fill slots 0.. in ascending order; the
-// other slots are marked free.
+// cumulative attention ("H2O Heavy-Hitter Oracle 分析", §3.1) — or, under Top-K
+// (blog §3.1.1: the highest current attention), the highest probability in the
+// prompt's last attention row, or, under a position policy (blog §3.1.1, §3.3 Q1),
+// the highest 0/1 position class. Ties rank the newer position higher, so the older
+// one is dropped. If T <= k every position is kept. Kept positions fill slots 0.. in
+// ascending order; the other slots are marked free. The seeded running score is the
+// column sum under every policy.
+//
+// last_row (Top-K only, before the seed): per unit, the logits of the last prompt
+// query against every prompt key, then their softmax, written as the seed scores.
 //
 // Selection: column sums are >= 0, so their fp32 bit patterns order like the
 // values. Four MSB-first radix passes (8-bit digits, 256-bin LDS histogram, a
@@ -178,9 +183,13 @@ __global__ __launch_bounds__(kThreads) void seed_kernel(SeedParams p) {
     const int ncand = T_ - p.k_local;
     // The ranking score of position j: the column sum under H2O and Top-K, a 0/1 position
     // class under the position policies.
+    // Under Top-K the scores come from the last-row kernel's array instead.
+    const float* rank = p.rank ? p.rank + (size_t)unit * Ts : nullptr;
     auto key = [&](int j) -> unsigned {
       float cj;
-      if constexpr (kLds) cj = __uint_as_float(bits[j]); else cj = c[j];
+      if (rank) cj = rank[j];
+      else if constexpr (kLds) cj = __uint_as_float(bits[j]);
+      else cj = c[j];
       return __float_as_uint(policy_seed(p.policy, p.policy_param, cj, j));
     };
 
@@ -329,6 +338,55 @@ __global__ __launch_bounds__(kThreads) void seed_kernel(SeedParams p) {
   }
 }
 
+// One workgroup per unit: s_j = q_{T-1} . k_j * log2(e) / sqrt(D) for every prompt key
+// (row groups of LANES lanes read one key row as 16-byte chunks), then M = max s,
+// L = sum 2^(s_j - M), P[T-1][j] = 2^(s_j - M) / L. The logits go through the rank array
+// itself; every sum runs in a fixed order.
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void last_row_kernel(LastRowParams p) {
+  constexpr int VEC = Chunk<T>::N, LANES = D / VEC, ROWS = kThreads / LANES;
+  __shared__ float s_red[kWaves];
+  const int unit = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rl = tid % LANES, g = tid / LANES;
+  const int Ts = p.T, T_ = unit_bound(p.lens, unit, p.heads, Ts, Ts);
+  if (T_ <= p.k_slots) return;                  // every position is kept: nothing to rank
+  const T* K = static_cast<const T*>(p.k) + (size_t)unit * Ts * D;
+  const T* Q = static_cast<const T*>(p.q) + ((size_t)unit * Ts + (T_ - 1)) * D;
+  float* rank = p.rank + (size_t)unit * Ts;
+  float qf[VEC];
+  load_f32(Q + rl * VEC, qf);
+
+  float m = -INFINITY;
+  for (int j0 = 0; j0 < T_; j0 += ROWS) {
+    const int j = j0 + g, jc = j < T_ ? j : 0;
+    float kf[VEC];
+    load_f32(K + (size_t)jc * D + rl * VEC, kf);
+    float d = 0.f;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) d = fmaf(qf[i], kf[i], d);
+    const float s = group_sum<LANES>(d) * p.qk_scale;
+    if (j < T_) {
+      if (rl == 0) rank[j] = s;
+      m = fmaxf(m, s);
+    }
+  }
+  auto block_fold = [&](float v, bool is_max) {
+    v = is_max ? group_max<kWave>(v) : group_sum<kWave>(v);
+    if (lane == 0) s_red[wave] = v;
+    __syncthreads();                            // also publishes the rank writes above
+    float r = s_red[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) r = is_max ? fmaxf(r, s_red[w]) : r + s_red[w];
+    __syncthreads();                            // s_red is reused by the next fold
+    return r;
+  };
+  const float M = block_fold(m, true);
+  float l = 0.f;
+  for (int j = tid; j < T_; j += kThreads) l += fast_exp2(rank[j] - M);
+  const float L = block_fold(l, false);
+  for (int j = tid; j < T_; j += kThreads) rank[j] = fast_exp2(rank[j] - M) / L;
+}
+
 __global__ void reset_kernel(ResetParams p) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < p.n; i += stride) {
@@ -357,6 +415,24 @@ hipError_t launch_seed(DType dt, bool f8, int D, const SeedParams& p, hipStream_
     case DType::F16: return D == 64 ? seed<_Float16, 64>(p, s) : seed<_Float16, 128>(p, s);
     default: return D == 64 ? seed<__bf16, 64>(p, s) : seed<__bf16, 128>(p, s);
   }
+}
+
+hipError_t launch_last_row(DType dt, int D, const LastRowParams& p, hipStream_t s) {
+  const dim3 grid((unsigned)p.units), block(kThreads);
+  switch (dt) {
+    case DType::F32:
+      if (D == 64) last_row_kernel<float, 64><<<grid, block, 0, s>>>(p);
+      else last_row_kernel<float, 128><<<grid, block, 0, s>>>(p);
+      break;
+    case DType::F16:
+      if (D == 64) last_row_kernel<_Float16, 64><<<grid, block, 0, s>>>(p);
+      else last_row_kernel<_Float16, 128><<<grid, block, 0, s>>>(p);
+      break;
+    default:
+      if (D == 64) last_row_kernel<__bf16, 64><<<grid, block, 0, s>>>(p);
+      else last_row_kernel<__bf16, 128><<<grid, block, 0, s>>>(p);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_reset(const ResetParams& p, hipStream_t s) {
