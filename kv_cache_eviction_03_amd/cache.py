@@ -60,6 +60,7 @@ class H2OCache:
         self.acc_score = torch.zeros((batch, heads, self.k), dtype=torch.float32,
                                      device=self.device)
         self.t = 0
+        self.t_seq = None          # per-sequence device positions, set by prefill_ragged
         self.workspace = torch.empty(0, dtype=torch.uint8, device=self.device)
         self.reserve(max_prompt)
 
@@ -159,6 +160,8 @@ class H2OCache:
             aux = DecodeAux(_ptr(victim_slot), _ptr(evicted_pos), _ptr(evicted_acc))
         ws = self.workspace
         tp = self.t_seq if t is None else t
+        if tp is None:
+            raise ValueError("decode_ragged: no positions (run prefill_ragged or pass t)")
         if tp.dtype != torch.int32 or tuple(tp.shape) != (self.batch,) or not tp.is_contiguous() \
                 or tp.device != self.device:
             raise ValueError(f"t: expected contiguous int32 ({self.batch},) on {self.device}")
@@ -171,11 +174,19 @@ class H2OCache:
         return out
 
     def state(self) -> dict:
-        """The whole cache state (for checkpoints): tensors plus the host counter t."""
-        return {"k_slots": self.k_slots, "v_slots": self.v_slots, "slot_pos": self.slot_pos,
-                "acc_score": self.acc_score, "t": self.t}
+        """The whole cache state (for checkpoints): tensors, the host counter t and, after a
+        ragged prefill, the per-sequence device positions t_seq."""
+        st = {"k_slots": self.k_slots, "v_slots": self.v_slots, "slot_pos": self.slot_pos,
+              "acc_score": self.acc_score, "t": self.t}
+        if getattr(self, "t_seq", None) is not None:
+            st["t_seq"] = self.t_seq
+        return st
 
     def load_state(self, st: dict) -> None:
         for name in ("k_slots", "v_slots", "slot_pos", "acc_score"):
             getattr(self, name).copy_(st[name])
         self.t = int(st["t"])
+        if st.get("t_seq") is not None:
+            self.t_seq = st["t_seq"].to(device=self.device, dtype=torch.int32).clone()
+        else:
+            self.t_seq = None
