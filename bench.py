@@ -1,47 +1,39 @@
 """Throughput of the H2O hot path on one MI355X, as one JSON line.
 
-Workload: the OPT-6.7B-shaped layer — batch 8, 32 heads, head_dim 128, fp16
-K/V, a 512-token padded prompt plus 32 generated tokens, k = 52 heavy + 52
-local slots (20% of the prompt). Inputs are seeded synthetic draws, generated
-on the device before timing.
+Workload (the headline): the LLaMA-7B-shaped stack — 32 layers, batch 64, 32 heads,
+head_dim 128, bf16 K/V, a 512-token padded prompt plus 1024 generated tokens, k = 52
+heavy + 52 local slots per (layer, sequence, head) (20% of the prompt). Inputs are
+seeded synthetic draws (5% heavy-hitter keys), generated on the device before timing.
 
-One step = one pass of the whole hot path over the batch: reset, prefill
-(causal attention + column sums + cache seeding) and 32 decode steps (fused
-attention + score accumulation + masked argmin + in-place overwrite). `value`
-is generated tokens per second of the whole step (batch * 32 / step time), the
-end-to-end token throughput the H2O blog's §3.1.3 defines; the decode-phase
-and prefill-phase rates are reported beside it.
+One step = one pass of the whole hot path over the batch: every layer's reset and
+prefill (causal attention + column sums + cache seeding), then 1024 model decode
+steps of 32 layer launches each (fused attention + score accumulation + masked argmin
++ in-place overwrite). `value` is generated tokens per second of the whole step
+(64 * 1024 / step time), the end-to-end token throughput the H2O blog's §3.1.3
+defines; the decode-phase and prefill-phase rates are reported beside it.
 
 Timing:
-  * timed loop: each step replays one HIP graph (reset, prefill, the 32 decode
-    launches), with HIP events around the loop, on torch's stream;
-  * phase split: a second loop replays the step as two graphs (reset+prefill, then
-    the 32 decode launches) with HIP events around each phase; the decode phase
-    divided by its 32 launches is the decode kernel's mean device duration used for
-    the roofline (it agrees with rocprofv3's kernel trace);
-  * graph replays are checked bit for bit against an eager run;
-  * cpu_baseline: the CPU oracle on the same inputs (all 256 units of one step);
+  * each step replays one HIP graph of the 32 layers' reset + prefill, then the decode
+    phase as graphs of G model steps each (positions are host arguments, so each graph
+    holds its own); HIP events on torch's stream around the timed loop and around each
+    phase;
+  * roofline: the decode kernel's mean device duration = decode phase time / its 32 * 1024
+    launches (graph gaps included: conservative), against its algorithmic bytes;
+  * graph replays are checked bit for bit against an eager run of the same step;
+  * cpu_baseline: the CPU oracle on 64 sampled (layer, sequence, head) units of the same
+    inputs (prefill + 1024 decode steps each), extrapolated to the whole step;
+  * opt67_layer: the OPT-6.7B-shaped layer (batch 8, fp16, prompt 512 + 32), whole step
+    as one graph, and its decode launch MALL-warm and MALL-cold;
   * prefill_mfma_opt30b: the prefill of the OPT-30B-shaped layer (T = 2048), where
     prefill is MFMA-bound, against the 2.5 PFLOP/s dense fp16 peak;
-  * decode_by_workload: the decode kernel at each workload's layer shape (the
-    LLaMA-7B layer, the OPT-30B layer, the 4096-slot stream), graph-replayed;
-  * roofline_cold: the bench workload's decode launch with the 256 MB Infinity Cache
-    out of play (36 replicas of the cache state visited in turn, 519 MB per sweep);
-  * dense_comparator: context only, the same decode steps with k = T + n (nothing
-    evicted) against the H2O budget;
-  * hbm_measured_ceiling: context only, plain PyTorch streaming read and copy rates;
-  * launch_floor: context only, the per-launch time of graph-replayed trivial kernels,
-    and the decode launch's bandwidth over the time it spends above that floor;
-  * ragged_step: the bench layer with seeded prompt lengths in [256, 512] through the
-    ragged entry points, against the same batch padded to 512;
-  * decode_by_workload_e4m3: the same shapes with FP8 E4M3 slots (half the slot bytes);
-  * decode_by_policy: the bench layer's decode launch under each eviction ranking;
-  * llama_stack_decode: the LLaMA-7B-shaped model's decode step, 32 layers each with
-    its own prefilled cache (3.69 GB of slots per step, far beyond the MALL);
-  * stream_sustained: the long-streaming workload in full (4096 slots, 2^20 decode
-    steps from an empty cache), device time per 65,536-step window after the fill; then
-    (graph_replayed) its first 4096 + 4 x 65,536 steps again as replays of one 256-step
-    HIP graph that advances its own positions, checked bit for bit against the direct run.
+  * decode_by_workload (+ _e4m3, + cold): the decode kernel at each workload's layer shape;
+  * hbm_measured_ceiling / mfma_measured_ceiling: the streaming-read and MFMA-loop probes
+    (libh2o_probes.so), plus plain PyTorch read and copy rates;
+  * dense_comparator, launch_floor, ragged_step, decode_by_policy: context figures;
+  * stream_sustained: the long-streaming workload in full (4096 slots, 2^20 decode steps
+    from an empty cache), and its first 4096 + 4 x 65,536 steps again as replays of one
+    256-step HIP graph, checked bit for bit against the direct run.
+Every timed figure is the median of its repetitions, with the min beside it.
 """
 from __future__ import annotations
 
@@ -58,14 +50,17 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published
 METRIC = "H2O decode tokens/s at 20% KV budget + % of HBM roofline (prefill % MFMA peak)"
 
-# HBM bytes per decode launch on this workload from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
-# runs of this script, scaled by the same counters on a plain 512 MiB copy
-# (`--copy-probe`). They describe one build of the decode kernel: the hash of its sources
-# is recorded with them, and the figure is reported only while the sources still match.
+# HBM bytes per decode launch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of this
+# script, scaled by the same counters on a plain 512 MiB copy (`--copy-probe`), per
+# workload. They describe one build of the decode kernel: the hash of its sources is
+# recorded with them, and a figure is reported only while the sources still match.
 DECODE_SOURCES = ("kv_cache_eviction_03_amd/csrc/decode.hip",
                   "kv_cache_eviction_03_amd/csrc/h2o_device.hpp")
-DECODE_TRAFFIC = {"sha256": "be2177095510c15d554060f1d93eb213918d04261518bacd574c49931b7fd80c",
-                  "read_bytes": 14174610, "write_bytes": 376832}
+DECODE_TRAFFIC = {
+    "opt-6.7b-layer-fp16": {"sha256": "be2177095510c15d554060f1d93eb213918d04261518bacd574c49931b7fd80c",
+                            "read_bytes": 14174610, "write_bytes": 376832},
+    "llama-7b-stack-bf16": {"sha256": None, "read_bytes": None, "write_bytes": None},
+}
 
 
 def decode_sources_hash() -> str:
@@ -77,11 +72,34 @@ def decode_sources_hash() -> str:
     return h.hexdigest()
 
 
-def decode_traffic():
-    t = DECODE_TRAFFIC
-    if t["sha256"] is None or t["sha256"] != decode_sources_hash():
+def decode_traffic(workload: str):
+    t = DECODE_TRAFFIC.get(workload)
+    if t is None or t["sha256"] is None or t["sha256"] != decode_sources_hash():
         return None
     return t["read_bytes"] + t["write_bytes"]
+
+
+def stats(times):
+    """Median and min of a list of per-call times (the figure is the median)."""
+    import statistics
+    return statistics.median(times), min(times)
+
+
+def replay_times(g, reps, per, before=None):
+    """Per-call times (us) of `reps` replays of graph g, each divided by `per` calls, with
+    HIP events on torch's current stream; `before` runs (untimed) ahead of each replay."""
+    import torch
+    out = []
+    for _ in range(reps):
+        if before is not None:
+            before()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        out.append(1e3 * a.elapsed_time(b) / per)
+    return out
 
 
 def decode_bytes_per_unit(w) -> int:
@@ -104,7 +122,8 @@ def prefill_bytes_per_unit(w) -> int:
 
 
 def prefill_mfma_probe(reps=10, warmup=3):
-    """Prefill of the OPT-30B-shaped layer (T = 2048, MFMA-bound) timed with HIP events."""
+    """Prefill of the OPT-30B-shaped layer (T = 2048, MFMA-bound) timed with HIP events,
+    one event pair per h2o_prefill call (median and min over `reps`)."""
     import torch
 
     from kv_cache_eviction_03_amd import H2OCache
@@ -115,27 +134,33 @@ def prefill_mfma_probe(reps=10, warmup=3):
                  max_prompt=w.prompt)
     out = torch.empty((w.batch, w.heads, w.prompt, w.head_dim), dtype=torch.float32, device="cuda:0")
     cs = torch.empty((w.batch, w.heads, w.prompt), dtype=torch.float32, device="cuda:0")
+
+    def call():
+        c.prefill(x["q_prompt"], x["k_prompt"], x["v_prompt"], out=out, colsum=cs)
     for _ in range(warmup):                     # the shader clock ramps over the first calls
-        c.prefill(x["q_prompt"], x["k_prompt"], x["v_prompt"], out=out, colsum=cs)
+        call()
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
+    times = []
     for _ in range(reps):
-        c.prefill(x["q_prompt"], x["k_prompt"], x["v_prompt"], out=out, colsum=cs)
-    b.record()
-    torch.cuda.synchronize()
-    us = 1e3 * a.elapsed_time(b) / reps
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        call()
+        b.record()
+        torch.cuda.synchronize()
+        times.append(1e3 * a.elapsed_time(b))
+    us, us_min = stats(times)
     flops = prefill_flops_per_unit(w) * w.units_per_layer
     tflops = flops / (us * 1e-6) / 1e12
     res = {"workload": f"{w.name}: batch {w.batch}, {w.heads} heads, d {w.head_dim}, fp16, "
                        f"prompt {w.prompt}, k = {w.k_heavy}+{w.k_local}",
            "bound": "mfma (arithmetic intensity %.0f flop/B > ridge 312.5)" % (
                prefill_flops_per_unit(w) / prefill_bytes_per_unit(w)),
-           "prefill_us": us, "achieved_tflops": tflops, "peak_tflops": MFMA_F16_PEAK_TFLOPS,
-           "frac": tflops / MFMA_F16_PEAK_TFLOPS,
+           "prefill_us": us, "prefill_us_min": us_min, "achieved_tflops": tflops,
+           "peak_tflops": MFMA_F16_PEAK_TFLOPS, "frac": tflops / MFMA_F16_PEAK_TFLOPS,
+           "frac_at_min": flops / (us_min * 1e-6) / 1e12 / MFMA_F16_PEAK_TFLOPS,
            "prompt_tokens_per_s": w.batch * w.prompt / (us * 1e-6),
            "note": "algorithmic flops 2T(T+1)d per unit over one h2o_prefill call "
-                   "(attention + column sums + seeding)"}
+                   "(attention + column sums + seeding); median of %d calls" % reps}
     del x, c, out, cs
     torch.cuda.empty_cache()
     return res
@@ -167,18 +192,13 @@ def decode_by_policy(n=32, reps=5):
                 for i in range(n):
                     c.decode(x["q_dec"][i], x["k_dec"][i], x["v_dec"][i], out=out[i])
         torch.cuda.synchronize()
-        best = None
-        for _ in range(reps):
+
+        def refill():
             c.reset()
             c.prefill(x["q_prompt"], x["k_prompt"], x["v_prompt"])
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            g.replay()
-            b.record()
-            torch.cuda.synchronize()
-            us = 1e3 * a.elapsed_time(b) / n
-            best = us if best is None else min(best, us)
-        res.append({"policy": policy, "policy_param": param, "us_per_launch": best})
+        us, us_min = stats(replay_times(g, reps, n, before=refill))
+        res.append({"policy": policy, "policy_param": param, "us_per_launch": us,
+                    "us_per_launch_min": us_min})
         del c, g
     del x, out
     torch.cuda.empty_cache()
@@ -189,8 +209,8 @@ def decode_by_workload(ids=(2, 3, 4, 5), n=32, reps=5, slot_format="input"):
     """Decode launches of each workload's layer shape, graph-replayed, timed with HIP events.
 
     The cache is filled by a prefill of k + 64 tokens (so every step evicts), then n
-    decode steps are captured once and replayed; the best replay's mean per launch is
-    reported with the algorithmic bytes of one launch. slot_format "e4m3" runs the same
+    decode steps are captured once and replayed; the median (and min) replay's mean per
+    launch is reported with the algorithmic bytes of one launch. slot_format "e4m3" runs the same
     shapes with FP8 E4M3 slots (scales 1: the synthetic K/V, heavy-hitter keys included,
     stay far inside the E4M3 range of +-448).
     """
@@ -217,87 +237,22 @@ def decode_by_workload(ids=(2, 3, 4, 5), n=32, reps=5, slot_format="input"):
                 for i in range(n):
                     c.decode(x["q_dec"][i], x["k_dec"][i], x["v_dec"][i], out=out[i])
         torch.cuda.synchronize()
-        best = None
-        for _ in range(reps):
+
+        def refill():
             c.reset()
             c.prefill(x["q_prompt"], x["k_prompt"], x["v_prompt"])
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            g.replay()
-            b.record()
-            torch.cuda.synchronize()
-            us = 1e3 * a.elapsed_time(b) / n
-            best = us if best is None else min(best, us)
+        us, us_min = stats(replay_times(g, reps, n, before=refill))
         byt = decode_bytes_per_unit(w) * w.units_per_layer
         slots = "e4m3 slots" if slot_format == "e4m3" else f"{w.dtype} slots"
         res.append({"workload": f"{w.name} layer: B {w.batch}, H {w.heads}, d {w.head_dim}, "
                                 f"{w.dtype} inputs, {slots}, k = {w.k_heavy}+{w.k_local}",
-                    "us_per_launch": best, "algorithmic_MB": byt / 1e6,
-                    "GBps": byt / (best * 1e-6) / 1e9, "hbm_frac": byt / (best * 1e-6) / 1e9 / HBM_PEAK_GBS,
-                    "decode_tokens_per_s": w.batch / (best * 1e-6)})
+                    "us_per_launch": us, "us_per_launch_min": us_min,
+                    "algorithmic_MB": byt / 1e6, "GBps": byt / (us * 1e-6) / 1e9,
+                    "hbm_frac": byt / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                    "hbm_frac_at_min": byt / (us_min * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                    "decode_tokens_per_s": w.batch / (us * 1e-6)})
         del x, c, out, g
         torch.cuda.empty_cache()
-    return res
-
-
-def llama_stack_decode(steps=16, reps=3):
-    """The LLaMA-7B-shaped stack in full: 32 layers (batch 64, 32 heads, d 128, bf16,
-    k = 52 + 52), each with its own cache prefilled from its own seeded 512-token prompt.
-    One decode step of the model runs the 32 layers' decode launches in turn, 3.69 GB of
-    slots per step (14x the MALL), so every launch reads its layer's slots from HBM.
-    `steps` such steps are captured as one graph; each timed replay starts from the saved
-    post-prefill state of every layer."""
-    import torch
-
-    from kv_cache_eviction_03_amd import H2OCache
-    from workloads import WORKLOADS, generate
-    dev = "cuda:0"
-    w = WORKLOADS[3].scaled(steps=steps)
-    caches, dec, snaps = [], [], []
-    for layer in range(w.layers):
-        x = generate(w, seed=0, layer=layer, device=dev)
-        c = H2OCache(w.batch, w.heads, w.head_dim, w.k_heavy, w.k_local, w.torch_dtype, dev,
-                     max_prompt=w.prompt)
-        c.reset()
-        c.prefill(x["q_prompt"], x["k_prompt"], x["v_prompt"], want_colsum=False)
-        caches.append(c)
-        dec.append((x["q_dec"], x["k_dec"], x["v_dec"]))
-        snaps.append({k: (v.clone() if torch.is_tensor(v) else v) for k, v in c.state().items()})
-        del x
-    torch.cuda.synchronize()
-    out = torch.empty((w.batch, w.heads, w.head_dim), dtype=torch.float32, device=dev)
-    side = torch.cuda.Stream(dev)
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(side):
-        with torch.cuda.graph(g, stream=side):
-            for i in range(steps):
-                for c, (q, k, v) in zip(caches, dec):
-                    c.decode(q[i], k[i], v[i], out=out)
-    torch.cuda.synchronize()
-    times = []
-    for _ in range(reps):
-        for c, st in zip(caches, snaps):
-            c.load_state(st)
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        g.replay()
-        b.record()
-        torch.cuda.synchronize()
-        times.append(1e3 * a.elapsed_time(b) / steps)
-    us = sorted(times)[len(times) // 2]
-    byt = decode_bytes_per_unit(w) * w.units_per_layer * w.layers
-    res = {"workload": f"{w.name}: {w.layers} layers, batch {w.batch}, {w.heads} heads, "
-                       f"d {w.head_dim}, bf16, prompt {w.prompt}, k = {w.k_heavy}+{w.k_local}",
-           "us_per_model_step": us, "us_per_model_step_best": min(times),
-           "us_per_layer_launch": us / w.layers,
-           "decode_tokens_per_s": w.batch / (us * 1e-6),
-           "algorithmic_GB_per_step": byt / 1e9,
-           "GBps": byt / (us * 1e-6) / 1e9, "hbm_frac": byt / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-           "note": f"{steps} model steps (x {w.layers} layer launches) as one graph, median of "
-                   f"{reps} replays from the saved post-prefill state; HIP events"}
-    del caches, dec, snaps, out, g
-    torch.cuda.empty_cache()
     return res
 
 
@@ -349,14 +304,9 @@ def ragged_step(reps=20, seed=7):
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(reps):
-            g.replay()
-        b.record()
-        torch.cuda.synchronize()
-        us = 1e3 * a.elapsed_time(b) / reps
-        res[mode] = {"us_per_step": us, "generated_tokens_per_s": B * n / (us * 1e-6)}
+        us, us_min = stats(replay_times(g, reps, 1))
+        res[mode] = {"us_per_step": us, "us_per_step_min": us_min,
+                     "generated_tokens_per_s": B * n / (us * 1e-6)}
         del c, g
     res["workload"] = (f"{w.name} shape with prompt lengths {lens.tolist()} (seeded uniform in "
                        f"[256, {T}], stored padded to {T}), {n} generated tokens each")
@@ -373,11 +323,9 @@ def decode_cold(w, replicas=36, reps=5):
     `replicas` independent caches, each prefilled from the same prompt, are visited in turn
     by one graph of `replicas` decode steps, so consecutive steps touch disjoint slot arrays
     and the state swept per replay (replicas x the step's bytes, >= 512 MB) is at least twice
-    the 256 MB MALL. The same launch shape as the warm figure; best and median replay, per
+    the 256 MB MALL. The same launch shape as the warm figure; median and best replay, per
     step. Replays repeat each replica's position t; that leaves the work per step unchanged.
     """
-    import statistics
-
     import torch
 
     from kv_cache_eviction_03_amd import H2OCache
@@ -402,16 +350,8 @@ def decode_cold(w, replicas=36, reps=5):
     torch.cuda.synchronize()
     g.replay()
     torch.cuda.synchronize()
-    per = []
-    for _ in range(reps):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        g.replay()
-        b.record()
-        torch.cuda.synchronize()
-        per.append(1e3 * a.elapsed_time(b) / replicas)
+    med, best = stats(replay_times(g, reps, replicas))
     byt = decode_bytes_per_unit(w) * w.units_per_layer
-    best, med = min(per), statistics.median(per)
     del x, caches, out, g
     torch.cuda.empty_cache()
     return {"workload": f"{w.name} layer: B {w.batch}, H {w.heads}, d {w.head_dim}, {w.dtype}, "
@@ -419,6 +359,7 @@ def decode_cold(w, replicas=36, reps=5):
             "bound": "hbm", "kernel": "decode step, MALL-cold",
             "achieved": byt / (med * 1e-6) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": byt / (med * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "frac_at_min": byt / (best * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "avg_launch_us": med, "best_launch_us": best,
             "algorithmic_bytes_per_launch": byt, "replicas": replicas,
             "state_swept_MB": replicas * byt / 1e6,
@@ -446,33 +387,50 @@ def launch_floor(w, n=32, reps=10):
                 for _ in range(n):
                     fn()
         torch.cuda.synchronize()
-        best = None
-        for _ in range(reps):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            g.replay()
-            b.record()
-            torch.cuda.synchronize()
-            us = 1e3 * a.elapsed_time(b) / n
-            best = us if best is None else min(best, us)
-        res[name] = best
+        res[name], res[name.replace("_us", "_us_min")] = stats(replay_times(g, reps, n))
         del g
     del x, c
     return res
 
 
-def hbm_ceiling(reps=10):
-    """Context: what plain PyTorch streaming kernels reach on this HBM (MALL-cold sizes):
-    a 1 GiB fp32 sum (read) and a 512 MiB copy (read + write). Median of `reps`."""
-    import statistics
+def _probe_lib():
+    import ctypes
+    from kv_cache_eviction_03_amd.build import PROBE_LIB
+    if not os.path.exists(PROBE_LIB):
+        raise RuntimeError(f"{PROBE_LIB} is not built; run `python -m kv_cache_eviction_03_amd.build`")
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.hbm_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                   ctypes.c_int, ctypes.c_void_p]
+    lib.hbm_read_probe.restype = ctypes.c_int
+    lib.mfma_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.mfma_probe.restype = ctypes.c_int
+    lib.mfma_probe_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.mfma_probe_flops.restype = ctypes.c_double
+    return lib
 
+
+def hbm_ceiling(reps=10):
+    """What this HBM delivers to a plain streaming read, MALL-cold (2 GiB, 8x the MALL):
+    the hand-written probe of libh2o_probes.so (16-byte loads, eight in flight per thread,
+    grid-stride, 2048 workgroups of 256 threads), and PyTorch's sum (read) and copy
+    (read + write) as context. Median and min of `reps` calls, HIP events per call."""
     import torch
-    n = (1 << 30) // 4
-    x = torch.ones(n, dtype=torch.float32, device="cuda:0")
-    y = torch.empty(n // 2, dtype=torch.float32, device="cuda:0")
+    lib = _probe_lib()
+    nbytes = 2 << 30
+    blocks = 2048
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    sink = torch.empty(blocks * 256, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def probe():
+        if lib.hbm_read_probe(buf.data_ptr(), nbytes, sink.data_ptr(), blocks, stream):
+            raise RuntimeError("hbm_read_probe refused its sizes or failed to launch")
+    half = buf[: nbytes // 8]
+    dst = torch.empty_like(half)
     out = {}
-    for name, fn, nbytes in (("read_GBps", lambda: x.sum(), 4 * n),
-                             ("copy_GBps", lambda: y.copy_(x[: n // 2]), 4 * n)):
+    for name, fn, moved in (("read_probe_GBps", probe, nbytes),
+                            ("torch_sum_GBps", lambda: buf.sum(), nbytes),
+                            ("torch_copy_GBps", lambda: dst.copy_(half), nbytes // 2)):
         fn()
         torch.cuda.synchronize()
         ts = []
@@ -483,11 +441,46 @@ def hbm_ceiling(reps=10):
             b.record()
             torch.cuda.synchronize()
             ts.append(a.elapsed_time(b) * 1e-3)
-        out[name] = nbytes / statistics.median(ts) / 1e9
-    del x, y
+        med, mn = stats(ts)
+        out[name] = moved / med / 1e9
+        out[name.replace("_GBps", "_GBps_max")] = moved / mn / 1e9
+    out["read_probe_frac_of_nominal"] = out["read_probe_GBps"] / HBM_PEAK_GBS
+    out["note"] = ("2 GiB read by the streaming-read probe and by torch sum; torch copy of "
+                   "512 MiB (1 GiB moved); medians (and best) of %d calls" % reps)
+    del buf, sink, half, dst
     torch.cuda.empty_cache()
-    out["note"] = "torch sum over 1 GiB fp32; torch copy of 512 MiB (1 GiB moved); medians"
     return out
+
+
+def mfma_ceiling(reps=5, iters=4096):
+    """The dense fp16 MFMA rate of a register-only loop (libh2o_probes.so: eight
+    independent 16x16x32 accumulation chains per wave, 256-thread workgroups, 8 per CU)."""
+    import torch
+    lib = _probe_lib()
+    blocks = 256 * 8
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def probe():
+        if lib.mfma_probe(blocks, iters, out.data_ptr(), stream):
+            raise RuntimeError("mfma_probe failed to launch")
+    probe()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        probe()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) * 1e-3)
+    med, mn = stats(ts)
+    flops = lib.mfma_probe_flops(blocks, iters)
+    del out
+    return {"fp16_TFLOPs": flops / med / 1e12, "fp16_TFLOPs_max": flops / mn / 1e12,
+            "frac_of_nominal": flops / med / 1e12 / MFMA_F16_PEAK_TFLOPS,
+            "note": f"{blocks} workgroups x 4 waves x {iters} rounds x 8 chains of "
+                    f"v_mfma_f32_16x16x32_f16; median (and best) of {reps} launches"}
 
 
 def decode_cold_by_workload(ids_replicas=((3, 5), (4, 3), (5, 8))):
@@ -499,7 +492,7 @@ def decode_cold_by_workload(ids_replicas=((3, 5), (4, 3), (5, 8))):
         w = WORKLOADS[wid].scaled(prompt=WORKLOADS[wid].k + 64, steps=1, layers=1)
         d = decode_cold(w, replicas=r)
         res.append({k: d[k] for k in ("workload", "avg_launch_us", "best_launch_us", "achieved",
-                                      "frac", "replicas", "state_swept_MB")})
+                                      "frac", "frac_at_min", "replicas", "state_swept_MB")})
     return res
 
 
@@ -527,21 +520,16 @@ def dense_comparator(w, reps=5):
             for i in range(n):
                 c.decode(x["q_dec"][i], x["k_dec"][i], x["v_dec"][i], out=out[i])
     torch.cuda.synchronize()
-    best = None
-    for _ in range(reps):
+
+    def refill():
         c.reset()
         c.prefill(x["q_prompt"], x["k_prompt"], x["v_prompt"])
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        g.replay()
-        b.record()
-        torch.cuda.synchronize()
-        us = 1e3 * a.elapsed_time(b) / n
-        best = us if best is None else min(best, us)
+    us, us_min = stats(replay_times(g, reps, n, before=refill))
     del x, c, out, g
     torch.cuda.empty_cache()
     return {"workload": f"{w.name} layer with k = T + n = {kd} (no eviction)",
-            "decode_us_per_step": best, "decode_tokens_per_s": w.batch / (best * 1e-6)}
+            "decode_us_per_step": us, "decode_us_per_step_min": us_min,
+            "decode_tokens_per_s": w.batch / (us * 1e-6)}
 
 
 def stream_sustained(window=65536, graph_windows=4, G=256):
@@ -690,71 +678,335 @@ def stream_graph(w, x, snap, steps, fill, window, G):
     return res
 
 
-def cpu_baseline(w, x, units, min_seconds=10.0):
+def cpu_baseline(w, units_inputs, total_units, min_seconds=10.0, single_core_units=8):
+    """The CPU oracle (as it stands) on sampled units of the headline workload: each unit is
+    a prompt plus every decode step of that (layer, sequence, head), independent of all
+    others, so the whole step's oracle time is the mean unit time times the number of units
+    (extrapolated linearly). units_inputs: host float64 inputs of the sampled units."""
     from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import run_unit
-    host = {k: v.double().cpu().numpy() for k, v in x.items()}
 
-    def timed(min_s, unit_list):
+    def timed(min_s, sample):
         # Whole passes over the sampled units until about min_s of CPU work has been timed.
         t0 = time.perf_counter()
         passes = 0
         while True:
-            for uidx in unit_list:
-                b, h = divmod(uidx, w.heads)
-                run_unit(w.k_heavy, w.k_local, host["q_prompt"][b, h], host["k_prompt"][b, h],
-                         host["v_prompt"][b, h], host["q_dec"][:, b, h], host["k_dec"][:, b, h],
-                         host["v_dec"][:, b, h])
+            for u in sample:
+                run_unit(w.k_heavy, w.k_local, u["Qp"], u["Kp"], u["Vp"], u["qd"], u["kd"],
+                         u["vd"])
             passes += 1
             dt = time.perf_counter() - t0
             if dt >= min_s or passes >= 50:
                 return dt, passes
 
     def rate(dt, passes, n_units):
-        return w.batch * w.steps / (dt / (passes * n_units) * w.units_per_layer)
+        return w.batch * w.steps / (dt / (passes * n_units) * total_units)
 
-    dt, passes = timed(min_seconds, units)
+    dt, passes = timed(min_seconds, units_inputs)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    few = units_inputs[:single_core_units]
     with threadpool_limits(limits=1):           # the same oracle on one core
-        few = units[: max(1, len(units) // 8)]
-        dt1, passes1 = timed(min_seconds / 2, few)
-    return {"value": rate(dt, passes, len(units)), "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{passes} pass(es) over {len(units)} of {w.units_per_layer} units (prefill + "
-                      f"{w.steps} decode steps each) in {dt:.1f} s, scaled to the whole step",
+        dt1, passes1 = timed(min_seconds / 4, few)
+    return {"value": rate(dt, passes, len(units_inputs)), "unit": "tokens/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"{passes} pass(es) over {len(units_inputs)} sampled (layer, sequence, head) "
+                      f"units of {total_units} (prompt {w.prompt} + {w.steps} decode steps each) "
+                      f"in {dt:.1f} s, extrapolated linearly to the whole step",
+            "extrapolated": True,
             "value_1_core": rate(dt1, passes1, len(few)),
-            "sample_1_core": f"{passes1} pass(es) over {len(few)} units in {dt1:.1f} s, one BLAS "
-                             f"thread, scaled to the whole step"}
+            "sample_1_core": f"{passes1} pass(es) over {len(few)} of those units in {dt1:.1f} s, "
+                             f"one BLAS thread, extrapolated to the whole step"}
+
+
+def opt67_layer(steps, warmup, seed=0, with_cold=True):
+    """The OPT-6.7B-shaped layer (batch 8, 32 heads, d 128, fp16, prompt 512 + 32, k = 52 +
+    52): one step (reset + prefill + 32 decode steps) replayed as one HIP graph, then the
+    same step as two graphs for the phase split; the decode phase's mean per launch is the
+    decode kernel's duration (MALL-warm: the 14 MB layer state stays in the Infinity
+    Cache), and with_cold adds the MALL-cold launch (36 replicas)."""
+    import torch
+
+    from kv_cache_eviction_03_amd import H2OCache
+    from workloads import WORKLOADS, generate
+    dev = torch.device("cuda:0")
+    w = WORKLOADS[2]
+    x = generate(w, seed=seed, device=dev)
+    B, H, d, T, n = w.batch, w.heads, w.head_dim, w.prompt, w.steps
+    units = w.units_per_layer
+    cache = H2OCache(B, H, d, w.k_heavy, w.k_local, w.torch_dtype, dev, max_prompt=T)
+    out_p = torch.empty((B, H, T, d), dtype=torch.float32, device=dev)
+    colsum = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    outs = torch.empty((n, B, H, d), dtype=torch.float32, device=dev)
+
+    def run_prefill():
+        cache.reset()
+        cache.prefill(x["q_prompt"], x["k_prompt"], x["v_prompt"], out=out_p, colsum=colsum)
+
+    def run_decode():
+        for i in range(n):
+            cache.decode(x["q_dec"][i], x["k_dec"][i], x["v_dec"][i], out=outs[i])
+
+    run_prefill()
+    run_decode()
+    torch.cuda.synchronize()
+    ref_state = {k: v.clone() for k, v in cache.state().items() if torch.is_tensor(v)}
+    ref_outs = outs.clone()
+    side = torch.cuda.Stream(dev)
+    g_step, g_pre, g_dec = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g_step, stream=side):
+            run_prefill()
+            run_decode()
+        with torch.cuda.graph(g_pre, stream=side):
+            run_prefill()
+        cache.t = T
+        with torch.cuda.graph(g_dec, stream=side):
+            run_decode()
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        g_step.replay()
+    torch.cuda.synchronize()
+    step_us, step_us_min = stats(replay_times(g_step, steps, 1))
+
+    def check_replay(what):
+        for k, v in ref_state.items():
+            if not torch.equal(getattr(cache, k), v):
+                raise RuntimeError(f"{what} replay diverged from the eager run in {k}")
+        if not torch.equal(outs, ref_outs):
+            raise RuntimeError(f"{what} replay diverged from the eager run in decode outputs")
+    check_replay("opt67 step graph")
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e0, e1, e2 in ev:
+        e0.record(stream)
+        g_pre.replay()
+        e1.record(stream)
+        g_dec.replay()
+        e2.record(stream)
+    torch.cuda.synchronize()
+    pre_us, pre_us_min = stats([1e3 * a.elapsed_time(b) for a, b, _ in ev])
+    dec_us, dec_us_min = stats([1e3 * b.elapsed_time(c) / n for _, b, c in ev])
+    check_replay("opt67 phase graph")
+    dec_bytes = decode_bytes_per_unit(w) * units
+    res = {"workload": f"{w.name}: batch {B}, {H} heads, head_dim {d}, fp16 K/V, prompt {T} + "
+                       f"{n} generated, k = {w.k_heavy} heavy + {w.k_local} local slots",
+           "us_per_step": step_us, "us_per_step_min": step_us_min,
+           "generated_tokens_per_s": B * n / (step_us * 1e-6),
+           "prefill_phase_us": pre_us, "prefill_phase_us_min": pre_us_min,
+           "prefill_tokens_per_s": B * T / (pre_us * 1e-6),
+           "decode_launch_us": dec_us, "decode_launch_us_min": dec_us_min,
+           "decode_tokens_per_s": B / (dec_us * 1e-6),
+           "roofline_warm": {"bound": "hbm",
+                             "kernel": "decode_resident_kernel<_Float16,128,256,false,7>",
+                             "achieved": dec_bytes / (dec_us * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s",
+                             "frac": dec_bytes / (dec_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                             "traffic": decode_traffic(w.name),
+                             "algorithmic_bytes_per_launch": dec_bytes,
+                             "note": "MALL-warm: the layer's 14 MB decode state stays in the "
+                                     "256 MB Infinity Cache between launches"},
+           "roofline_prefill": {
+               "bound": "hbm (arithmetic intensity %.1f flop/B < ridge 312.5)" % (
+                   prefill_flops_per_unit(w) / prefill_bytes_per_unit(w)),
+               "mfma_frac": prefill_flops_per_unit(w) * units / (pre_us * 1e-6) / 1e12
+               / MFMA_F16_PEAK_TFLOPS,
+               "hbm_frac": prefill_bytes_per_unit(w) * units / (pre_us * 1e-6) / 1e9
+               / HBM_PEAK_GBS}}
+    floor = launch_floor(w)
+    above = dec_us - floor["h2o_reset_us"]
+    floor["decode_us_above_floor"] = above
+    floor["decode_GBps_above_floor"] = dec_bytes / (above * 1e-6) / 1e9 if above > 0 else None
+    res["launch_floor"] = floor
+    del g_step, g_pre, g_dec, cache, x, out_p, colsum, outs
+    torch.cuda.empty_cache()
+    if with_cold:
+        res["roofline_cold"] = decode_cold(w)
+        res["roofline_cold"]["kernel"] = ("decode_resident_kernel<_Float16,128,256,false,7>, "
+                                          "MALL-cold")
+        dense = dense_comparator(w)
+        dense["h2o_decode_speedup"] = dense["decode_us_per_step"] / dec_us
+        res["dense_comparator"] = dense
+    return res
+
+
+HEADLINE_KERNEL = "decode_resident_kernel<__bf16,128,256,false,7>"
+
+
+def headline_stack(steps, warmup, seed=0, per_graph=64, cpu_units=64, cpu_seconds=10.0):
+    """The LLaMA-7B-shaped stack end to end (see the module docstring). Returns the result
+    fields of the JSON line that describe the headline."""
+    import torch
+
+    from kv_cache_eviction_03_amd import H2OStack
+    from workloads import WORKLOADS, generate, sample_units
+    dev = torch.device("cuda:0")
+    w = WORKLOADS[3]
+    B, H, d, T, n, L = w.batch, w.heads, w.head_dim, w.prompt, w.steps, w.layers
+    units = w.units_per_layer
+    print(f"[bench] headline {w.name}: generating {L} layers' inputs", file=sys.stderr, flush=True)
+    xs = [generate(w, seed=seed, layer=l, device=dev) for l in range(L)]
+    prompts = [(x["q_prompt"], x["k_prompt"], x["v_prompt"]) for x in xs]
+    dec = [(x["q_dec"], x["k_dec"], x["v_dec"]) for x in xs]
+    st = H2OStack(L, B, H, d, w.k_heavy, w.k_local, w.torch_dtype, dev, max_prompt=T)
+    out_p = torch.empty((B, H, T, d), dtype=torch.float32, device=dev)
+    outs = [torch.empty((B, H, d), dtype=torch.float32, device=dev) for _ in range(L)]
+
+    # Eager reference run of one whole step (also warms the kernels up).
+    print("[bench] headline: eager reference step", file=sys.stderr, flush=True)
+    st.prefill(prompts, out_p)
+    for i in range(n):
+        st.decode_step(dec, i, outs)
+    torch.cuda.synchronize()
+    names = ("k_slots", "v_slots", "slot_pos", "acc_score")
+    ref = [{nm: getattr(c, nm).clone() for nm in names} for c in st.caches]
+    ref_outs = [o.clone() for o in outs]
+    ref_prefill = out_p.clone()
+
+    print("[bench] headline: capturing graphs", file=sys.stderr, flush=True)
+    g_pre = st.capture_prefill(prompts, out_p)
+    g_dec = st.capture_decode_run(dec, T, n, per_graph, outs)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(warmup):
+        g_pre.replay()
+        for g in g_dec:
+            g.replay()
+    torch.cuda.synchronize()
+
+    # Timed loop: exactly `steps` whole steps, events around the loop and each phase.
+    print(f"[bench] headline: timing {steps} steps", file=sys.stderr, flush=True)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for e0, e1, e2 in ev:
+        e0.record(stream)
+        g_pre.replay()
+        e1.record(stream)
+        for g in g_dec:
+            g.replay()
+        e2.record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms_per_step = start.elapsed_time(end) / steps
+    pre_ms = [a.elapsed_time(b) for a, b, _ in ev]
+    dec_ms = [b.elapsed_time(c) for _, b, c in ev]
+
+    # The replays must reproduce the eager run bit for bit.
+    for l, c in enumerate(st.caches):
+        for nm in names:
+            if not torch.equal(getattr(c, nm), ref[l][nm]):
+                raise RuntimeError(f"graph replay diverged from the eager run: layer {l} {nm}")
+        if not torch.equal(outs[l], ref_outs[l]):
+            raise RuntimeError(f"graph replay diverged from the eager run: layer {l} outputs")
+    if not torch.equal(out_p, ref_prefill):
+        raise RuntimeError("graph replay diverged from the eager run: prefill output")
+
+    launches = n * L
+    dec_launch_us, dec_launch_us_min = stats([1e3 * m / launches for m in dec_ms])
+    pre_med, pre_min = stats(pre_ms)
+    dec_med, dec_min = stats(dec_ms)
+    dec_bytes = decode_bytes_per_unit(w) * units
+    dec_gbs = dec_bytes / (dec_launch_us * 1e-6) / 1e9
+    pre_flops = prefill_flops_per_unit(w) * units * L
+    pre_bytes = prefill_bytes_per_unit(w) * units * L
+    res = {
+        "value": B * n / (ms_per_step * 1e-3),
+        "ms_per_step": ms_per_step,
+        "config": {
+            "workload": f"{w.name}: {L} layers, batch {B}, {H} heads, head_dim {d}, bf16 K/V, "
+                        f"prompt {T} + {n} generated, k = {w.k_heavy} heavy + {w.k_local} local "
+                        f"slots per (layer, sequence, head), 5% heavy-hitter keys",
+            "step": f"reset + prefill of all {L} layers (one graph), then {n} model decode steps "
+                    f"x {L} layer launches ({len(g_dec)} graphs of {per_graph} model steps)",
+            "value_is": "generated tokens / step time (prefill + decode)",
+            "global_batch": B, "seq_len": T + n, "parallelism": "single GPU",
+        },
+        "decode_tokens_per_s": B * n / (dec_med * 1e-3),
+        "prefill_tokens_per_s": B * T / (pre_med * 1e-3),
+        "phase_ms": {"prefill": pre_med, "prefill_min": pre_min,
+                     "decode": dec_med, "decode_min": dec_min},
+        "roofline": {
+            "bound": "hbm", "kernel": HEADLINE_KERNEL,
+            "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": dec_gbs / HBM_PEAK_GBS,
+            "frac_at_min": dec_bytes / (dec_launch_us_min * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "traffic": decode_traffic(w.name),
+            "avg_launch_us": dec_launch_us, "avg_launch_us_min": dec_launch_us_min,
+            "algorithmic_bytes_per_launch": dec_bytes,
+            "duration_from": f"HIP events around each step's decode phase ({launches} "
+                             f"graph-replayed launches), median over the timed steps",
+            "note": "every launch reads its layer's slots from HBM: a model step sweeps "
+                    f"{decode_bytes_per_unit(w) * units * L / 1e9:.2f} GB, 14x the 256 MB MALL",
+        },
+        "roofline_prefill": {
+            "bound": "hbm (arithmetic intensity %.1f flop/B < ridge 312.5)" % (
+                prefill_flops_per_unit(w) / prefill_bytes_per_unit(w)),
+            "achieved_tflops": pre_flops / (pre_med * 1e-3) / 1e12,
+            "mfma_peak_tflops": MFMA_F16_PEAK_TFLOPS,
+            "mfma_frac": pre_flops / (pre_med * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS,
+            "achieved_gbs": pre_bytes / (pre_med * 1e-3) / 1e9,
+            "hbm_frac": pre_bytes / (pre_med * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "note": f"prefill phase = {L} x (reset + attention with column sums + seed), "
+                    "algorithmic flops 2T(T+1)d and bytes per unit",
+        },
+        "wall_s_timed_loop": wall,
+    }
+    # Host copies of the sampled units for the oracle (64 of the L * B * H units, the first
+    # and the last always among them).
+    flat = sample_units(L * units, cpu_units, seed=seed)
+    f = lambda t: t.double().cpu().numpy()
+    sample = []
+    for u in flat:
+        l, r = divmod(u, units)
+        b, h = divmod(r, H)
+        x = xs[l]
+        sample.append({"Qp": f(x["q_prompt"][b, h]), "Kp": f(x["k_prompt"][b, h]),
+                       "Vp": f(x["v_prompt"][b, h]), "qd": f(x["q_dec"][:, b, h]),
+                       "kd": f(x["k_dec"][:, b, h]), "vd": f(x["v_dec"][:, b, h])})
+    del xs, prompts, dec, st, out_p, outs, ref, ref_outs, ref_prefill, g_pre, g_dec
+    torch.cuda.empty_cache()
+    return res, w, sample, L * units
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--graph-steps", type=int, default=64,
+                    help="model decode steps per captured graph of the headline")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="only the headline step (no extras, no CPU baseline): for profiling")
+    ap.add_argument("--cpu-units", type=int, default=64,
+                    help="sampled units the CPU oracle runs for cpu_baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mfma-probe", action="store_true")
     ap.add_argument("--decode-shapes", action="store_true",
                     help="only time the decode kernel at each workload's layer shape")
     ap.add_argument("--no-decode-shapes", action="store_true")
     ap.add_argument("--decode-cold", action="store_true",
-                    help="only time the bench workload's decode kernel with the MALL out of play")
+                    help="only the MALL-cold decode launches of every layer shape")
     ap.add_argument("--no-cold", action="store_true")
-    ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-stream", action="store_true",
                     help="skip the 2^20-step long-streaming run")
     ap.add_argument("--no-ragged", action="store_true",
-                    help="skip the ragged-batch step")
+                    help="skip the ragged-batch step and the policy launches")
+    ap.add_argument("--opt67-only", action="store_true",
+                    help="only the OPT-6.7B-shaped layer step; print its figures")
     ap.add_argument("--ragged-only", action="store_true",
-                    help="only the ragged-batch step; print its figures")
-    ap.add_argument("--no-stack", action="store_true",
-                    help="skip the 32-layer LLaMA-7B-shaped stack decode")
-    ap.add_argument("--stack-only", action="store_true",
-                    help="only the 32-layer LLaMA-7B-shaped stack decode; print its figures")
+                    help="only the ragged-batch step and the policy launches")
     ap.add_argument("--stream-only", action="store_true",
                     help="only the 2^20-step long-streaming run; print its figures")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="only the OPT-30B-shaped prefill; print its figures")
+    ap.add_argument("--ceilings-only", action="store_true",
+                    help="only the HBM and MFMA probes; print their figures")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 512 MiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -774,204 +1026,75 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 3}))
         return
-
     if args.decode_shapes:
         for r in decode_by_workload():
             print(json.dumps(r), flush=True)
         for r in decode_by_workload(slot_format="e4m3"):
             print(json.dumps(r), flush=True)
         return
+    if args.decode_cold:
+        from workloads import WORKLOADS
+        print(json.dumps(decode_cold(WORKLOADS[2])), flush=True)
+        for r in decode_cold_by_workload():
+            print(json.dumps(r), flush=True)
+        return
     if args.stream_only:
         print(json.dumps(stream_sustained()), flush=True)
-        return
-    if args.stack_only:
-        print(json.dumps(llama_stack_decode()), flush=True)
         return
     if args.ragged_only:
         print(json.dumps(ragged_step()), flush=True)
         print(json.dumps(decode_by_policy()), flush=True)
         return
-
-    from kv_cache_eviction_03_amd import H2OCache
-    from workloads import WORKLOADS, generate
-
-    w = WORKLOADS[2]
-    if args.decode_cold:
-        print(json.dumps(decode_cold(w)), flush=True)
-        for r in decode_cold_by_workload():
-            print(json.dumps(r), flush=True)
+    if args.opt67_only:
+        print(json.dumps(opt67_layer(max(args.steps, 5), args.warmup)), flush=True)
         return
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    x = generate(w, seed=args.seed, device=dev)
-    B, H, d, T, n = w.batch, w.heads, w.head_dim, w.prompt, w.steps
-    units = w.units_per_layer
+    if args.prefill_only:
+        print(json.dumps(prefill_mfma_probe()), flush=True)
+        return
+    if args.ceilings_only:
+        print(json.dumps({"hbm": hbm_ceiling(), "mfma": mfma_ceiling()}), flush=True)
+        return
 
-    cache = H2OCache(B, H, d, w.k_heavy, w.k_local, w.torch_dtype, dev, max_prompt=T)
-    out_p = torch.empty((B, H, T, d), dtype=torch.float32, device=dev)
-    colsum = torch.empty((B, H, T), dtype=torch.float32, device=dev)
-    outs = torch.empty((n, B, H, d), dtype=torch.float32, device=dev)
-
-    def run_prefill():
-        cache.reset()
-        cache.prefill(x["q_prompt"], x["k_prompt"], x["v_prompt"], out=out_p, colsum=colsum)
-
-    def run_decode():
-        for i in range(n):
-            cache.decode(x["q_dec"][i], x["k_dec"][i], x["v_dec"][i], out=outs[i])
-
-    # Eager reference run (also warms up the kernels).
-    run_prefill()
-    run_decode()
-    torch.cuda.synchronize()
-    ref_state = {k: v.clone() for k, v in cache.state().items() if torch.is_tensor(v)}
-    ref_outs = outs.clone()
-
-    # Capture the whole step as one HIP graph (the timed loop), and each phase as a graph
-    # of its own (a second loop, for the phase split and the decode kernel's duration).
-    side = torch.cuda.Stream(dev)
-    g_step, g_pre, g_dec = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-    with torch.cuda.stream(side):
-        with torch.cuda.graph(g_step, stream=side):
-            run_prefill()
-            run_decode()
-        with torch.cuda.graph(g_pre, stream=side):
-            run_prefill()
-        cache.t = T
-        with torch.cuda.graph(g_dec, stream=side):
-            run_decode()
-    torch.cuda.synchronize()
-
-    stream = torch.cuda.current_stream(dev)
-    for _ in range(args.warmup):
-        g_step.replay()
-    torch.cuda.synchronize()
-
-    # Timed loop: exactly `steps` replays of the whole step.
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(args.steps):
-        g_step.replay()
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall
-    total_ms = start.elapsed_time(end)
-    ms_per_step = total_ms / args.steps
-
-    # Graph replays must reproduce the eager run bit for bit.
-    def check_replay(what):
-        for k, v in ref_state.items():
-            if not torch.equal(getattr(cache, k), v):
-                raise RuntimeError(f"{what} replay diverged from the eager run in {k}")
-        if not torch.equal(outs, ref_outs):
-            raise RuntimeError(f"{what} replay diverged from the eager run in decode outputs")
-    check_replay("step graph")
-
-    # Phase split: the same step as two graphs with events between them.
-    for _ in range(args.warmup):
-        g_pre.replay()
-        g_dec.replay()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for e0, e1, e2 in ev:
-        e0.record(stream)
-        g_pre.replay()
-        e1.record(stream)
-        g_dec.replay()
-        e2.record(stream)
-    torch.cuda.synchronize()
-    pre_ms = sum(a.elapsed_time(b) for a, b, _ in ev) / args.steps
-    dec_ms = sum(b.elapsed_time(c) for _, b, c in ev) / args.steps
-    check_replay("phase graph")
-
-    # Decode phase = n back-to-back decode launches inside one graph: its mean per launch is
-    # the decode kernel's device duration (inter-node gaps included, so conservative).
-    dec_kernel_us = 1e3 * dec_ms / n
-    pre_call_us = 1e3 * pre_ms
-
-    dec_bytes = decode_bytes_per_unit(w) * units
-    dec_gbs = dec_bytes / (dec_kernel_us * 1e-6) / 1e9
-    pre_flops = prefill_flops_per_unit(w) * units
-    pre_tflops = pre_flops / (pre_call_us * 1e-6) / 1e12
-    pre_gbs = prefill_bytes_per_unit(w) * units / (pre_call_us * 1e-6) / 1e9
-
-    tokens = B * n
-    value = tokens / (ms_per_step * 1e-3)
+    torch.cuda.set_device(0)
+    head, w, sample, total_units = headline_stack(args.steps, args.warmup, seed=args.seed,
+                                                  per_graph=args.graph_steps,
+                                                  cpu_units=args.cpu_units)
     result = {
         "metric": METRIC,
-        "value": value,
+        "value": head["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": "bf16",
         "data": "synthetic",
-        "config": {
-            "workload": f"{w.name}: batch {B}, {H} heads, head_dim {d}, fp16 K/V, prompt {T} + "
-                        f"{n} generated, k = {w.k_heavy} heavy + {w.k_local} local slots",
-            "step": f"reset + prefill ({T} tokens) + {n} decode steps, replayed as one HIP graph",
-            "value_is": "generated tokens / step time (prefill + decode)",
-            "global_batch": B, "seq_len": T + n, "parallelism": "single GPU",
-        },
-        "decode_tokens_per_s": tokens / (dec_ms * 1e-3),
-        "prefill_tokens_per_s": B * T / (pre_ms * 1e-3),
-        "phase_ms": {"prefill": pre_ms, "decode": dec_ms},
-        "roofline": {
-            "bound": "hbm",
-            "kernel": "decode_resident_kernel<_Float16,128,256,false,7> (one launch per decode step)",
-            "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": dec_gbs / HBM_PEAK_GBS, "traffic": decode_traffic(),
-            "avg_launch_us": dec_kernel_us, "algorithmic_bytes_per_launch": dec_bytes,
-            "duration_from": "HIP events around the graph-replayed decode phase / launches",
-        },
-        "roofline_prefill": {
-            "bound": "hbm (arithmetic intensity %.1f flop/B < ridge 312.5)" % (
-                prefill_flops_per_unit(w) / prefill_bytes_per_unit(w)),
-            "achieved_tflops": pre_tflops, "mfma_peak_tflops": MFMA_F16_PEAK_TFLOPS,
-            "mfma_frac": pre_tflops / MFMA_F16_PEAK_TFLOPS,
-            "achieved_gbs": pre_gbs, "hbm_frac": pre_gbs / HBM_PEAK_GBS,
-            "avg_phase_us": pre_call_us,
-            "note": "prefill phase = reset + attention-with-column-sums + seed kernels",
-        },
-        "wall_s_timed_loop": wall,
     }
-    floor = launch_floor(w)
-    above = dec_kernel_us - floor["h2o_reset_us"]
-    floor["decode_us_above_floor"] = above
-    floor["decode_GBps_above_floor"] = dec_bytes / (above * 1e-6) / 1e9 if above > 0 else None
-    result["launch_floor"] = floor
-    if not args.no_mfma_probe:
-        result["prefill_mfma_opt30b"] = prefill_mfma_probe()
-    if not args.no_decode_shapes:
-        result["decode_by_workload"] = decode_by_workload()
-        result["decode_by_workload_e4m3"] = decode_by_workload(slot_format="e4m3")
-    if not args.no_cold:
+    result.update({k: v for k, v in head.items() if k not in result})
+    if not args.headline_only:
+        print("[bench] extras", file=sys.stderr, flush=True)
+        result["opt67_layer"] = opt67_layer(20, 3, with_cold=not args.no_cold)
+        if not args.no_mfma_probe:
+            result["prefill_mfma_opt30b"] = prefill_mfma_probe()
         result["hbm_measured_ceiling"] = hbm_ceiling()
-        result["roofline_cold"] = decode_cold(w)
-        result["roofline_cold"]["kernel"] = "decode_resident_kernel<_Float16,128,256,false,7>, MALL-cold"
+        result["mfma_measured_ceiling"] = mfma_ceiling()
         if not args.no_decode_shapes:
-            result["decode_cold_by_workload"] = decode_cold_by_workload()
-    if not args.no_dense:
-        dense = dense_comparator(w)
-        dense["h2o_decode_speedup"] = dense["decode_us_per_step"] / dec_kernel_us
-        result["dense_comparator"] = dense
-    if not args.no_ragged:
-        result["ragged_step"] = ragged_step()
-        result["decode_by_policy"] = decode_by_policy()
-    if not args.no_stack:
-        result["llama_stack_decode"] = llama_stack_decode()
-    if not args.no_stream:
-        result["stream_sustained"] = stream_sustained()
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, x, list(range(units)))
+            result["decode_by_workload"] = decode_by_workload()
+            result["decode_by_workload_e4m3"] = decode_by_workload(slot_format="e4m3")
+            if not args.no_cold:
+                result["decode_cold_by_workload"] = decode_cold_by_workload()
+        if not args.no_ragged:
+            result["ragged_step"] = ragged_step()
+            result["decode_by_policy"] = decode_by_policy()
+        if not args.no_stream:
+            result["stream_sustained"] = stream_sustained()
+        if not args.no_cpu_baseline:
+            print("[bench] cpu baseline", file=sys.stderr, flush=True)
+            result["cpu_baseline"] = cpu_baseline(w, sample, total_units,
+                                                  min_seconds=args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

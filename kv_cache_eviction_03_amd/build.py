@@ -2,7 +2,7 @@
 
 Usage: python -m kv_cache_eviction_03_amd.build   (or __graft_entry__.build())
 Always recompiles. Objects go to kv_cache_eviction_03_amd/_build/, the shared
-library next to this file.
+libraries (libh2o.so, and the measurement probes libh2o_probes.so) next to this file.
 """
 from __future__ import annotations
 
@@ -17,6 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libh2o.so")
+PROBE_LIB = os.path.join(HERE, "libh2o_probes.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -44,19 +45,27 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(OUT_DIR, exist_ok=True)
-    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(sources))) as ex:
-        objs = list(ex.map(_compile, sources))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    """libh2o.so from csrc/*.hip, and the measurement probes (csrc/probes/*.hip, the HBM
+    read and MFMA ceilings bench.py reports) as libh2o_probes.so."""
+    os.makedirs(OUT_DIR, exist_ok=True)
+    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    probes = sorted(glob.glob(os.path.join(CSRC, "probes", "*.hip")))
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(sources) + len(probes))) as ex:
+        objs = list(ex.map(_compile, sources + probes))
+    _link(objs[:len(sources)], LIB)
+    _link(objs[len(sources):], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

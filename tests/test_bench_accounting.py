@@ -23,8 +23,13 @@ def test_decode_bytes_per_unit_step():
     assert bench.decode_bytes_per_unit(WORKLOADS[4]) == 216_640
     # the 4096-slot stream, bf16: 2097152 + 49152 + 768 + 512 + 512 + 8
     assert bench.decode_bytes_per_unit(WORKLOADS[5]) == 2_148_104
-    # one launch of the bench layer moves 256 units' worth
+    # one launch of the OPT-6.7B layer moves 256 units' worth
     assert bench.decode_bytes_per_unit(WORKLOADS[2]) * WORKLOADS[2].units_per_layer == 14_411_776
+    # one launch of a LLaMA-7B layer (the headline's decode kernel) moves 2048 units' worth,
+    # a model step 32 launches
+    w = WORKLOADS[3]
+    assert bench.decode_bytes_per_unit(w) * w.units_per_layer == 115_294_208
+    assert bench.decode_bytes_per_unit(w) * w.units_per_layer * w.layers == 3_689_414_656
 
 
 def test_decode_bytes_with_e4m3_slots():
@@ -48,3 +53,6 @@ def test_prefill_work_per_unit():
     # arithmetic intensity above the 312.5 flop/B ridge of 2.5 PFLOP/s over 8 TB/s
     assert bench.prefill_flops_per_unit(w) / bench.prefill_bytes_per_unit(w) > 312.5
     assert bench.prefill_flops_per_unit(WORKLOADS[2]) / bench.prefill_bytes_per_unit(WORKLOADS[2]) < 312.5
+    # the headline's 32-layer prefill: 2048 units per layer
+    w = WORKLOADS[3]
+    assert bench.prefill_flops_per_unit(w) * w.units_per_layer * w.layers == 4_406_636_445_696          # 67,239,936 x 65,536
