@@ -400,13 +400,16 @@ def _probe_lib():
         raise RuntimeError(f"{PROBE_LIB} is not built; run `python -m kv_cache_eviction_03_amd.build`")
     lib = ctypes.CDLL(PROBE_LIB)
     lib.hbm_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
-                                   ctypes.c_int, ctypes.c_void_p]
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.hbm_read_probe.restype = ctypes.c_int
     lib.mfma_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     lib.mfma_probe.restype = ctypes.c_int
     lib.mfma_probe_flops.argtypes = [ctypes.c_int, ctypes.c_int]
     lib.mfma_probe_flops.restype = ctypes.c_double
     return lib
+
+
+PROBE_LAYOUT = 1      # whole 32 KB tiles per workgroup (the fastest layout measured)
 
 
 def hbm_ceiling(reps=10):
@@ -423,14 +426,15 @@ def hbm_ceiling(reps=10):
     stream = torch.cuda.current_stream().cuda_stream
 
     def probe():
-        if lib.hbm_read_probe(buf.data_ptr(), nbytes, sink.data_ptr(), blocks, stream):
+        if lib.hbm_read_probe(buf.data_ptr(), nbytes, sink.data_ptr(), blocks, PROBE_LAYOUT,
+                              stream):
             raise RuntimeError("hbm_read_probe refused its sizes or failed to launch")
-    half = buf[: nbytes // 8]
+    half = buf[: nbytes // 8]                   # 1 GiB: a copy reads it and writes 1 GiB
     dst = torch.empty_like(half)
     out = {}
     for name, fn, moved in (("read_probe_GBps", probe, nbytes),
                             ("torch_sum_GBps", lambda: buf.sum(), nbytes),
-                            ("torch_copy_GBps", lambda: dst.copy_(half), nbytes // 2)):
+                            ("torch_copy_GBps", lambda: dst.copy_(half), nbytes)):
         fn()
         torch.cuda.synchronize()
         ts = []
@@ -446,7 +450,7 @@ def hbm_ceiling(reps=10):
         out[name.replace("_GBps", "_GBps_max")] = moved / mn / 1e9
     out["read_probe_frac_of_nominal"] = out["read_probe_GBps"] / HBM_PEAK_GBS
     out["note"] = ("2 GiB read by the streaming-read probe and by torch sum; torch copy of "
-                   "512 MiB (1 GiB moved); medians (and best) of %d calls" % reps)
+                   "1 GiB (2 GiB moved); medians (and best) of %d calls" % reps)
     del buf, sink, half, dst
     torch.cuda.empty_cache()
     return out

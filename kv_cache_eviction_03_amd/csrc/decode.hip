@@ -46,6 +46,13 @@ namespace h2o {
 namespace {
 
 constexpr int kBatch = 8;         // slot rows per row group in one load batch
+// Slot rows (16-bit input slots) are read with nontemporal loads: each is read once per
+// step, and a deep model visits every other layer before it comes back to this one.
+constexpr bool kSlotNT = true;
+__device__ __forceinline__ uint4 ld_slot(const void* p) { return kSlotNT ? ld16_nt(p) : ld16(p); }
+// 256-thread launches with more units than this take the two-phase resident kernel: about
+// what the one-phase kernel (five workgroups per CU at 84 VGPRs) holds at once on 256 CUs.
+constexpr int kTwoPhaseUnits = 1024;
 // The split partial kernel's: 7 makes 37 chunks of 112 slots for the 4096-slot stream
 // instead of 33 of 128 (the last holding one slot), 17.4 -> 17.1 us per step.
 constexpr int kPartBatch = 7;
@@ -80,17 +87,26 @@ __device__ __forceinline__ void load_rows(const typename SlotChunk<T, F8>::elem*
                                           typename SlotChunk<T, F8>::type (&vr)[U]) {
   using S = Shape<T, D, THREADS>;
   using SC = SlotChunk<T, F8>;
+  if constexpr (F8) {
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int j = first + u * S::ROWS;
-    const bool slot = j < n;
-    const size_t off = (size_t)(slot ? j : 0) * D + rl * S::VEC;
-    if constexpr (F8) {
+    for (int u = 0; u < U; ++u) {
+      const int j = first + u * S::ROWS;
+      const size_t off = (size_t)(j < n ? j : 0) * D + rl * S::VEC;
       kr[u] = SC::load(ks + off);
       vr[u] = SC::load(vs + off);
-    } else {
-      kr[u] = ld16(slot ? ks + off : kn + rl * S::VEC);
-      vr[u] = ld16(slot ? vs + off : vn + rl * S::VEC);
+    }
+  } else {
+    // One base address per lane and a constant step per slot (row u is a valid slot when
+    // first < n - u * ROWS, a compare against a uniform value): fewer live address
+    // registers than one offset per slot (OPT-6.7B and LLaMA-7B shapes: 84 -> 77 VGPRs).
+    const size_t off = (size_t)first * D + rl * S::VEC;
+    const T* kb = ks + off;
+    const T* vb = vs + off;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool slot = first < n - u * S::ROWS;
+      kr[u] = ld_slot(slot ? kb + u * S::ROWS * D : kn + rl * S::VEC);
+      vr[u] = ld_slot(slot ? vb + u * S::ROWS * D : vn + rl * S::VEC);
     }
   }
 }
@@ -195,7 +211,17 @@ __device__ __forceinline__ uint64_t score_key(float a, int pos) {
 
 // ------------------------------------------------------------------ resident --
 
-template <typename T, int D, int THREADS, bool F8, int UB = kBatch>
+// Component-wise select of 16-byte chunks (a select of whole vectors can be lowered
+// through private memory).
+__device__ __forceinline__ uint4 sel16(bool c, const uint4& a, const uint4& b) {
+  return make_uint4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
+}
+
+template <typename T, int D, int THREADS, bool F8, int UB = kBatch, bool TP = false>
+// TP (two phases, 16-bit input slots only): the K rows are loaded and turned into logits
+// before the V rows are loaded into the same registers, and the new token's row reaches
+// the store through LDS, so a lane holds one set of slot chunks instead of two (at most 64
+// VGPRs: eight waves per SIMD, the LLaMA-7B layer's 2048 workgroups all resident at once).
 // UB slots per row group: kBatch, or 7 for 16-bit inputs when k + 1 <= 7 row groups' worth
 // (the k = 104 caches of the OPT-6.7B and LLaMA-7B layers need 105 of the 112 slots; the
 // OPT-30B layer's 411 need 7 of 8 at 1024 threads): one load and one logit fewer per lane.
@@ -210,13 +236,15 @@ template <typename T, int D, int THREADS, bool F8, int UB = kBatch>
 // with seven). The cap with eight slots spilled and measured slower on the 256-thread
 // shape (12.5 -> 15.8 us on the LLaMA-7B layer).
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(
-    THREADS == 256 ? (UB == 7 && F8 ? 8 : 4) : (F8 ? 8 : 1), 8)))
+    TP ? 8 : (THREADS == 256 ? (UB == 7 && F8 ? 8 : 4) : (UB == 7 && F8 ? 8 : 1)), 8)))
 void decode_resident_kernel(DecodeParams p) {
   using S = Shape<T, D, THREADS>;
   using SC = SlotChunk<T, F8>;
   using SE = typename SC::elem;
   constexpr int VEC = S::VEC, LANES = S::LANES, ROWS = S::ROWS, U = UB;
   static_assert(U <= LANES, "a lane owns one slot score");
+  static_assert(!(TP && (F8 || sizeof(T) != 2)), "two-phase loads take 16-bit input slots");
+  __shared__ uint4 s_new[2][TP ? LANES : 1];     // TP: the new token's K and V rows
   __shared__ __attribute__((aligned(16))) float s_red[ROWS * D];
   __shared__ float s_m[ROWS], s_l[ROWS];
   __shared__ float s_logit[ROWS * U];
@@ -238,38 +266,106 @@ void decode_resident_kernel(DecodeParams p) {
   int32_t* pos = p.slot_pos + (size_t)unit * k;
   float* acc = p.acc + (size_t)unit * k;
 
-  // Every load of the unit, issued before any is consumed.
+  // Every load of the unit (with TP: every K load), issued before any is consumed.
   const uint4 qr = ld16(static_cast<const T*>(p.q) + (size_t)unit * D + rl * VEC);
   typename SC::type kr[U], vr[U];
-  load_rows<T, D, U, THREADS, F8>(ks, vs, kn, vn, g, n, rl, kr, vr);
+  // TP: one base address per lane and a constant step per slot, row u valid when
+  // g < n - u * ROWS (a compare against a uniform value), rows past the valid slots read
+  // the new token's row.
+  const size_t lane_off = (size_t)g * D + rl * VEC;
+  if constexpr (TP) {
+    const SE* kb = ks + lane_off;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      kr[u] = ld_slot(g < n - u * ROWS ? kb + u * ROWS * D : kn + rl * VEC);
+  } else {
+    load_rows<T, D, U, THREADS, F8>(ks, vs, kn, vn, g, n, rl, kr, vr);
+  }
   const int jo = rl * ROWS + g;                 // slot whose score this lane owns
   const bool own = rl < U && jo < n;
   const int jc = own ? jo : 0;
   const float acc_old = acc[jc];
   const int pos_old = pos[jc];
-  const uint4 knr = ld16(kn + rl * VEC), vnr = ld16(vn + rl * VEC);
+  uint4 knr, vnr;
+  if constexpr (!TP) {
+    knr = ld16(kn + rl * VEC);
+    vnr = ld16(vn + rl * VEC);
+  }
   __builtin_amdgcn_sched_barrier(0);            // keep every load ahead of the math
 
-  // The new token's row as it will be stored.
+  // The new token's row as it will be stored (TP: read back from LDS at the store).
   typename SC::type kst, vst;
   if constexpr (F8) {
     kst = quant_e4m3<T>(knr, p.k_inv);
     vst = quant_e4m3<T>(vnr, p.v_inv);
     fill_new_rows<T, D, U, THREADS>(g, n, kst, vst, kr, vr);
-  } else {
+  } else if constexpr (!TP) {
     kst = knr;
     vst = vnr;
   }
   float s[U], mg, lg, o[VEC];
-  group_softmax<T, D, U, THREADS>(qr, p.qk_scale, kr, vr, g, n, s, mg, lg, o);
+  if constexpr (TP) {
+    // Row n (the new token) sits in row group n % ROWS at u = n / ROWS (k + 1 <= U * ROWS).
+    const int un = n / ROWS;
+    const bool gn = g == n % ROWS;
+    mg = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float d = row_sum<LANES>(chunk_dot(qr, kr[u], 0.f, T{})) * p.qk_scale;
+      s[u] = g <= n - u * ROWS ? d : -INFINITY;
+      mg = fmaxf(mg, s[u]);
+    }
+    if (gn) {
+      uint4 x = kr[0];
+#pragma unroll
+      for (int u = 1; u < U; ++u) x = sel16(u == un, kr[u], x);
+      s_new[0][rl] = x;
+    }
+    if (rl == 0) {                              // the logits are staged now: s[] turns into
+#pragma unroll                                  // the weights below
+      for (int u = 0; u < U; ++u) s_logit[u * ROWS + g] = s[u];
+    }
+    __builtin_amdgcn_sched_barrier(0);          // the V loads reuse the K registers
+    const SE* vb = vs + lane_off;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      vr[u] = ld_slot(g < n - u * ROWS ? vb + u * ROWS * D : vn + rl * VEC);
+    const float mref = mg == -INFINITY ? 0.f : mg;
+    lg = 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {               // the weights, while the V rows are in flight
+      s[u] = fast_exp2(s[u] - mref);
+      lg += s[u];
+    }
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) o[i] = 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float vf[VEC];
+      unpack(vr[u], vf, T{});
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) o[i] = fmaf(s[u], vf[i], o[i]);
+    }
+    __builtin_amdgcn_sched_barrier(0);          // the copy below waits for every V row
+    if (gn) {
+      uint4 x = vr[0];
+#pragma unroll
+      for (int u = 1; u < U; ++u) x = sel16(u == un, vr[u], x);
+      s_new[1][rl] = x;
+    }
+  } else {
+    group_softmax<T, D, U, THREADS>(qr, p.qk_scale, kr, vr, g, n, s, mg, lg, o);
+  }
 
 #pragma unroll
   for (int i = 0; i < VEC; ++i) s_red[g * D + rl * VEC + i] = o[i];
   if (rl == 0) {
     s_m[g] = mg;
     s_l[g] = lg;
+    if constexpr (!TP) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) s_logit[u * ROWS + g] = s[u];
+      for (int u = 0; u < U; ++u) s_logit[u * ROWS + g] = s[u];
+    }
   }
   __syncthreads();                              // (1) every K/V read is consumed
   // Scale factors 2^(m_g - M) of the row groups, formed by every wave for itself with
@@ -338,6 +434,10 @@ void decode_resident_kernel(DecodeParams p) {
     meta = jo == n;
   }
   if (dst >= 0) {
+    if constexpr (TP) {
+      kst = s_new[0][rl];
+      vst = s_new[1][rl];
+    }
     SC::store(ks + (size_t)dst * D + rl * VEC, kst);
     SC::store(vs + (size_t)dst * D + rl * VEC, vst);
   }
@@ -606,7 +706,14 @@ hipError_t run(const DecodeParams& p, const SplitScratch& w, hipStream_t s) {
     if (plan.threads == 256) {
       if constexpr (sizeof(T) == 2) {
         if (p.k + 1 <= Shape<T, D, 256>::ROWS * 7) {
-          decode_resident_kernel<T, D, 256, F8, 7><<<dim3(p.units), dim3(256), 0, s>>>(p);
+          // Two phases only where the one-phase kernel (five workgroups per CU) cannot hold
+          // every unit at once: with fewer units the extra round trip costs more than it
+          // saves (OPT-6.7B layer, 256 units: 4.32 -> 4.57 us; LLaMA-7B layer, 2048 units:
+          // 19.7 -> 19.4 us, and 23.3 -> 22.5 us per launch in the 32-layer stack).
+          if (!F8 && p.units > kTwoPhaseUnits)
+            decode_resident_kernel<T, D, 256, F8, 7, !F8><<<dim3(p.units), dim3(256), 0, s>>>(p);
+          else
+            decode_resident_kernel<T, D, 256, F8, 7><<<dim3(p.units), dim3(256), 0, s>>>(p);
           return hipGetLastError();
         }
       }
@@ -615,7 +722,9 @@ hipError_t run(const DecodeParams& p, const SplitScratch& w, hipStream_t s) {
     else {
       if constexpr (sizeof(T) == 2) {
         if (p.k + 1 <= Shape<T, D, 1024>::ROWS * 7) {
-          decode_resident_kernel<T, D, 1024, F8, 7><<<dim3(p.units), dim3(1024), 0, s>>>(p);
+          // Two phases at 1024 threads: two workgroups per CU instead of one (OPT-30B layer,
+          // 896 units: 38.2 -> 31.0 us warm, 49.5 -> 41.3 us MALL-cold).
+          decode_resident_kernel<T, D, 1024, F8, 7, !F8><<<dim3(p.units), dim3(1024), 0, s>>>(p);
           return hipGetLastError();
         }
       }

@@ -26,6 +26,13 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 template <typename T> struct Chunk { static constexpr int N = 16 / sizeof(T); };
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+// The same load marked nontemporal (streamed, not kept in the caches): data read once per
+// kernel, such as a decode step's slot rows.
+__device__ __forceinline__ uint4 ld16_nt(const void* p) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(x[0], x[1], x[2], x[3]);
+}
 __device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 
 // Unpack a 16-byte chunk of T into fp32.

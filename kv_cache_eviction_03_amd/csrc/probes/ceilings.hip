@@ -2,10 +2,12 @@
 // dense MFMA loop. Measurement probes only (libh2o_probes.so); the H2O path never calls
 // them.
 //
-// hbm_read_probe: every thread reads 16-byte chunks, UNROLL loads in flight, grid-stride
-// over the buffer, and folds them into one word that it stores (so no load is dead). The
-// buffer must be a whole number of 16 * UNROLL * threads-per-grid chunks: the host call
-// checks that, and every load address is below `bytes`.
+// hbm_read_probe: every thread reads 16-byte chunks, UNROLL loads in flight, and folds
+// them into one word that it stores (so no load is dead). Layout 0 strides the whole grid
+// between a thread's loads; layout 1 gives each workgroup whole 32 KB tiles (a wave's loads
+// fall in one tile); layout 2 is layout 1 with nontemporal loads. The buffer must be a
+// whole number of 16 * UNROLL * threads-per-grid chunks: the host call checks that, and
+// every load address is below `bytes`.
 //
 // mfma_probe: every wave runs `iters` rounds of CHAINS independent 16x16x32 fp16 MFMA
 // accumulations (independent chains hide the MFMA latency) on register operands, and
@@ -19,17 +21,38 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kUnroll = 8;
 
+template <int LAYOUT>
 __global__ __launch_bounds__(kThreads) void hbm_read_kernel(const uint4* __restrict__ buf,
                                                            size_t chunks, uint32_t* sink) {
-  const size_t stride = (size_t)gridDim.x * kThreads;
-  size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  const size_t threads = (size_t)gridDim.x * kThreads;
   uint32_t acc = 0;
-  for (; i + (kUnroll - 1) * stride < chunks; i += kUnroll * stride) {
-    uint4 v[kUnroll];
+  if constexpr (LAYOUT == 0) {
+    for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i + (kUnroll - 1) * threads < chunks;
+         i += kUnroll * threads) {
+      uint4 v[kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) v[u] = buf[i + u * stride];
+      for (int u = 0; u < kUnroll; ++u) v[u] = buf[i + u * threads];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+      for (int u = 0; u < kUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+  } else {
+    constexpr size_t tile = (size_t)kThreads * kUnroll;          // chunks per tile
+    for (size_t t = blockIdx.x; (t + 1) * tile <= chunks; t += gridDim.x) {
+      const uint4* p = buf + t * tile + threadIdx.x;
+      uint4 v[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        if constexpr (LAYOUT == 2) {
+          typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+          const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + u * kThreads));
+          v[u] = make_uint4(x[0], x[1], x[2], x[3]);
+        } else {
+          v[u] = p[u * kThreads];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
   }
   sink[(size_t)blockIdx.x * kThreads + threadIdx.x] = acc;
 }
@@ -63,13 +86,19 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(int iters, float* out) {
 extern "C" {
 
 // Reads `bytes` of `buf` (device memory, 16-byte aligned) with `blocks` workgroups of 256
-// threads; `sink` holds blocks * 256 words. Returns 0, or -1 when the sizes do not fit the
-// kernel's unrolled loop exactly (then nothing is launched), or the HIP error code.
-int hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, int blocks, void* stream) {
+// threads in the given layout (0, 1 or 2); `sink` holds blocks * 256 words. Returns 0, or
+// -1 when an argument is out of range or the sizes do not fit the kernel's unrolled loop
+// exactly (then nothing is launched), or the HIP error code.
+int hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, int blocks, int layout,
+                   void* stream) {
   const size_t per_pass = (size_t)16 * kUnroll * kThreads * (size_t)blocks;
   if (!buf || !sink || blocks < 1 || bytes == 0 || bytes % per_pass != 0) return -1;
-  hbm_read_kernel<<<dim3(blocks), dim3(kThreads), 0, static_cast<hipStream_t>(stream)>>>(
-      static_cast<const uint4*>(buf), bytes / 16, sink);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const uint4* b = static_cast<const uint4*>(buf);
+  if (layout == 0) hbm_read_kernel<0><<<dim3(blocks), dim3(kThreads), 0, s>>>(b, bytes / 16, sink);
+  else if (layout == 1) hbm_read_kernel<1><<<dim3(blocks), dim3(kThreads), 0, s>>>(b, bytes / 16, sink);
+  else if (layout == 2) hbm_read_kernel<2><<<dim3(blocks), dim3(kThreads), 0, s>>>(b, bytes / 16, sink);
+  else return -1;
   return (int)hipGetLastError();
 }
 
