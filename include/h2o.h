@@ -204,8 +204,8 @@ size_t h2o_workspace_bytes(const h2o_cache_desc* cache, int32_t max_prompt);
  *               contract above)
  * Seeding (H2O blog §2.2; analysis page §3.1): if T <= k every position is
  * kept; otherwise the last k_local positions plus the k_heavy positions of
- * [0, T - k_local) with the highest fp32 c_j (ties: the newer position ranks
- * higher) are kept. Kept positions fill slots 0.. in ascending position order
+ * [0, T - k_local) with the highest fp32 seed score (c_j under H2O; see
+ * h2o_policy for the others; ties: the newer position ranks higher) are kept. Kept positions fill slots 0.. in ascending position order
  * (K/V rows copied from k and v, slot_pos = position, acc_score = fp32 c_j);
  * every other slot is marked free. All previous slot contents are replaced.
  * Returns H2O_ERR_UNSUPPORTED when one unit's prompt rows exceed 2^31 - 1 bytes
@@ -276,6 +276,27 @@ h2o_status h2o_decode_step_ragged(const h2o_cache_desc* cache, const int32_t* t,
                                   const void* k_new, const void* v_new, float* out,
                                   const h2o_decode_aux* aux, void* workspace,
                                   size_t workspace_bytes, void* stream);
+
+/*
+ * h2o_decode_step_noalloc - h2o_decode_step for callers that cannot allocate
+ * device memory or pass a workspace: code under HIP graph capture, serving
+ * loops that must not allocate, harnesses that forbid it. Same arguments,
+ * results and checks as h2o_decode_step without workspace / workspace_bytes;
+ * the same kernels run. It allocates nothing: the scratch that a decode
+ * spreading a unit's slots over several workgroups needs lives in a static
+ * device array of H2O_NOALLOC_SCRATCH_BYTES bytes that the library holds on
+ * each GPU it runs on until the process ends. A shape that needs more
+ * (h2o_workspace_bytes(cache, 0) > H2O_NOALLOC_SCRATCH_BYTES) returns
+ * H2O_ERR_UNSUPPORTED and enqueues nothing. The stream must belong to the
+ * current device (else H2O_ERR_INVALID). Every call on one GPU shares that
+ * GPU's array (its contents on entry never matter), so calls that can overlap
+ * on one GPU — on different streams, or from different threads — race and
+ * give undefined results; order them on one stream.
+ */
+#define H2O_NOALLOC_SCRATCH_BYTES (8u << 20)
+h2o_status h2o_decode_step_noalloc(const h2o_cache_desc* cache, int64_t t, const void* q,
+                                   const void* k_new, const void* v_new, float* out,
+                                   const h2o_decode_aux* aux, void* stream);
 
 /* Static string naming a status code. */
 const char* h2o_status_str(h2o_status status);

@@ -22,8 +22,11 @@ H2O_SLOTS_INPUT, H2O_SLOTS_FP8_E4M3 = range(2)
 SLOT_FORMAT_CODES = {"input": H2O_SLOTS_INPUT, "e4m3": H2O_SLOTS_FP8_E4M3}
 H2O_MAX_SLOTS = 8192
 
+H2O_NOALLOC_SCRATCH_BYTES = 8 << 20
+
 EXPORTS = ("h2o_reset", "h2o_workspace_bytes", "h2o_prefill", "h2o_decode_step",
-           "h2o_prefill_ragged", "h2o_decode_step_ragged", "h2o_status_str", "h2o_last_error")
+           "h2o_prefill_ragged", "h2o_decode_step_ragged", "h2o_decode_step_noalloc",
+           "h2o_status_str", "h2o_last_error")
 
 
 class CacheDesc(ctypes.Structure):
@@ -77,6 +80,9 @@ def library() -> ctypes.CDLL:
                                                c_void_p, c_void_p, P(DecodeAux), c_void_p,
                                                c_size_t, c_void_p]
         lib.h2o_decode_step_ragged.restype = c_int32
+        lib.h2o_decode_step_noalloc.argtypes = [P(CacheDesc), c_int64, c_void_p, c_void_p,
+                                                c_void_p, c_void_p, P(DecodeAux), c_void_p]
+        lib.h2o_decode_step_noalloc.restype = c_int32
         lib.h2o_status_str.argtypes = [c_int32]
         lib.h2o_status_str.restype = c_char_p
         lib.h2o_last_error.argtypes = []
@@ -120,6 +126,13 @@ def h2o_decode_step_ragged(desc: CacheDesc, t: int, q: int, k_new: int, v_new: i
     return library().h2o_decode_step_ragged(ctypes.byref(desc), t or None, q, k_new, v_new, out,
                                             ctypes.byref(aux) if aux is not None else None,
                                             workspace or None, workspace_bytes, stream)
+
+
+def h2o_decode_step_noalloc(desc: CacheDesc, t: int, q: int, k_new: int, v_new: int, out: int,
+                            aux: DecodeAux | None, stream: int) -> int:
+    return library().h2o_decode_step_noalloc(ctypes.byref(desc), t, q, k_new, v_new, out,
+                                             ctypes.byref(aux) if aux is not None else None,
+                                             stream)
 
 
 def h2o_status_str(status: int) -> str:

@@ -10,6 +10,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/h2o.h"
 #include "h2o_kernels.hpp"
@@ -120,6 +121,41 @@ float inv_of(const h2o_cache_desc* c, float scale) { return f8_of(c) ? 1.0f / sc
 
 float qk_scale(int d) { return (float)(1.4426950408889634 / std::sqrt((double)d)); }
 
+// Scratch of h2o_decode_step_noalloc: a file-scope device array (each GPU the library runs
+// on holds its own copy until the process ends). Host code uses the array's device address
+// from hipGetSymbolAddress, taken once per device with that device current; the array's
+// name in host code is only a host-side stand-in.
+static __device__ __align__(256) unsigned char scratch[H2O_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of the current device's scratch; the stream must belong to that
+// device.
+h2o_status noalloc_scratch(void** out, hipStream_t stream) {
+  int dev = -1;
+  if (hipError_t e = hipGetDevice(&dev)) return hip_fail(e, "hipGetDevice");
+  if (stream) {
+    int sdev = -1;
+    if (hipError_t e = hipStreamGetDevice(stream, &sdev)) return hip_fail(e, "hipStreamGetDevice");
+    if (sdev != dev)
+      return fail(H2O_ERR_INVALID, "the stream belongs to device %d but device %d is current",
+                  sdev, dev);
+  }
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(H2O_ERR_UNSUPPORTED, "device %d beyond the %d the scratch table holds", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)))
+      return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return H2O_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -218,11 +254,12 @@ h2o_status prefill_impl(const h2o_cache_desc* c, const void* q, const void* k, c
   return H2O_OK;
 }
 
-// The decode step behind both entry points; tpos = NULL means every sequence is at t.
+// The decode step behind the entry points; tpos = NULL means every sequence is at t.
+// noalloc: the scratch is the library's static array instead of the caller's workspace.
 h2o_status decode_impl(const h2o_cache_desc* c, int64_t t, const int32_t* tpos, const void* q,
                        const void* k_new, const void* v_new, float* out,
                        const h2o_decode_aux* aux, void* workspace, size_t workspace_bytes,
-                       void* stream) {
+                       void* stream, bool noalloc = false) {
   g_err[0] = 0;
   if (h2o_status st = check_desc(c)) return st;
   if (t < 0 || t >= (int64_t)H2O_MAX_POSITION)
@@ -245,11 +282,22 @@ h2o_status decode_impl(const h2o_cache_desc* c, int64_t t, const int32_t* tpos, 
     return fail(H2O_ERR_UNSUPPORTED, "batch * heads * %d decode workgroups exceed the grid limit",
                 plan.splits);
   const size_t scratch = decode_scratch(c);
-  if (scratch > 0 && (!workspace || workspace_bytes < scratch))
-    return fail(H2O_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
-                workspace ? workspace_bytes : (size_t)0, scratch);
-  if (workspace && !aligned(workspace, kWsAlign))
-    return fail(H2O_ERR_INVALID, "workspace must be %zu-byte aligned", kWsAlign);
+  if (noalloc) {
+    if (scratch > (size_t)H2O_NOALLOC_SCRATCH_BYTES)
+      return fail(H2O_ERR_UNSUPPORTED,
+                  "this shape needs %zu bytes of decode scratch; the static scratch of the "
+                  "allocation-free entry point holds %zu",
+                  scratch, (size_t)H2O_NOALLOC_SCRATCH_BYTES);
+  } else {
+    if (scratch > 0 && (!workspace || workspace_bytes < scratch))
+      return fail(H2O_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
+                  workspace ? workspace_bytes : (size_t)0, scratch);
+    if (workspace && !aligned(workspace, kWsAlign))
+      return fail(H2O_ERR_INVALID, "workspace must be %zu-byte aligned", kWsAlign);
+  }
+  // Every argument is checked; only now does the allocation-free path ask for its scratch.
+  if (noalloc && scratch > 0)
+    if (h2o_status st = noalloc_scratch(&workspace, static_cast<hipStream_t>(stream))) return st;
 
   const int D = c->head_dim;
   const int32_t kk = c->k_heavy + c->k_local;
@@ -296,6 +344,12 @@ h2o_status h2o_decode_step(const h2o_cache_desc* c, int64_t t, const void* q, co
                            void* workspace, size_t workspace_bytes, void* stream) {
   return decode_impl(c, t, nullptr, q, k_new, v_new, out, aux, workspace, workspace_bytes,
                      stream);
+}
+
+h2o_status h2o_decode_step_noalloc(const h2o_cache_desc* c, int64_t t, const void* q,
+                                   const void* k_new, const void* v_new, float* out,
+                                   const h2o_decode_aux* aux, void* stream) {
+  return decode_impl(c, t, nullptr, q, k_new, v_new, out, aux, nullptr, 0, stream, true);
 }
 
 h2o_status h2o_decode_step_ragged(const h2o_cache_desc* c, const int32_t* t, const void* q,

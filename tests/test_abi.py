@@ -150,6 +150,30 @@ def test_decode_checks(args, status):
 
 
 @pytest.mark.parametrize("args,status", [
+    (dict(t=-1), h2o.H2O_ERR_INVALID),
+    (dict(q=0), h2o.H2O_ERR_INVALID),
+    (dict(out=A + 4), h2o.H2O_ERR_INVALID),
+    (dict(aux=DecodeAux(0, 0, A + 1)), h2o.H2O_ERR_INVALID),
+    (dict(desc=dict(k_local=0)), h2o.H2O_ERR_INVALID),
+    (dict(desc=dict(head_dim=96)), h2o.H2O_ERR_UNSUPPORTED),
+    # a split decode whose scratch exceeds the static array (8192 slots, 300 units of fp32)
+    (dict(desc=dict(batch=100, heads=3, k_heavy=8000, k_local=192, dtype=h2o.H2O_F32)),
+     h2o.H2O_ERR_UNSUPPORTED),
+])
+def test_decode_noalloc_checks(args, status):
+    # Every check of h2o_decode_step, and the static scratch's limit, before any HIP call.
+    a = dict(t=10, q=A, k_new=A, v_new=A, out=A, aux=None, desc={})
+    a.update(args)
+    st = h2o.h2o_decode_step_noalloc(desc(**a["desc"]), a["t"], a["q"], a["k_new"], a["v_new"],
+                                     a["out"], a["aux"], 0)
+    assert st == status, h2o.h2o_last_error()
+    if status == h2o.H2O_ERR_UNSUPPORTED and "batch" in a["desc"]:
+        need = h2o.h2o_workspace_bytes(desc(**a["desc"]), 0)
+        assert need > h2o.H2O_NOALLOC_SCRATCH_BYTES
+        assert "static scratch" in h2o.h2o_last_error()
+
+
+@pytest.mark.parametrize("args,status", [
     (dict(lens=0), h2o.H2O_ERR_INVALID),
     (dict(lens=A + 2), h2o.H2O_ERR_INVALID),
     (dict(T=-1), h2o.H2O_ERR_INVALID),
