@@ -32,6 +32,8 @@
 // nearest-even E4M3 codes), 8 codes per 16-byte chunk of the prompt row.
 //
 // reset: slot_pos = -1, acc = 0 (blog §2.3: freeing a slot only marks it).
+#include <type_traits>
+
 #include "h2o_device.hpp"
 #include "h2o_kernels.hpp"
 
@@ -175,21 +177,20 @@ __global__ __launch_bounds__(kThreads) void seed_kernel(SeedParams p) {
     n_keep = T_;
     for (int s = tid; s < T_; s += kThreads) slot_of[s] = s;
   } else {
-    // The selection reads the column sums from the LDS stage or from global memory; the
-    // two are separate instantiations, so every read is a plain LDS or global load (a
-    // runtime choice between the two pointers would make them generic-address loads).
-    auto select = [&](auto from_lds) -> int {
-    constexpr bool kLds = decltype(from_lds)::value;
+    // The selection reads its scores from the LDS stage (SRC 0), the column sums in global
+    // memory (SRC 1) or, under Top-K, the last-row kernel's array (SRC 2); each source is
+    // an instantiation of its own, so every read is a plain LDS or global load (a runtime
+    // choice between the pointers would make them generic-address loads).
+    auto select = [&](auto src_c) -> int {
+    constexpr int SRC = decltype(src_c)::value;
     const int ncand = T_ - p.k_local;
-    // The ranking score of position j: the column sum under H2O and Top-K, a 0/1 position
-    // class under the position policies.
-    // Under Top-K the scores come from the last-row kernel's array instead.
-    const float* rank = p.rank ? p.rank + (size_t)unit * Ts : nullptr;
+    const float* rank = SRC == 2 ? p.rank + (size_t)unit * Ts : nullptr;
+    // The ranking score of position j (a 0/1 position class under the position policies).
     auto key = [&](int j) -> unsigned {
       float cj;
-      if (rank) cj = rank[j];
-      else if constexpr (kLds) cj = __uint_as_float(bits[j]);
-      else cj = c[j];
+      if constexpr (SRC == 0) cj = __uint_as_float(bits[j]);
+      else if constexpr (SRC == 1) cj = c[j];
+      else cj = rank[j];
       return __float_as_uint(policy_seed(p.policy, p.policy_param, cj, j));
     };
 
@@ -294,7 +295,9 @@ __global__ __launch_bounds__(kThreads) void seed_kernel(SeedParams p) {
     }
     return running < k ? running : k;
     };
-    n_keep = staged ? select(std::true_type{}) : select(std::false_type{});
+    n_keep = p.rank ? select(std::integral_constant<int, 2>{})
+             : staged ? select(std::integral_constant<int, 0>{})
+                      : select(std::integral_constant<int, 1>{});
   }
   __syncthreads();
 
