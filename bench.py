@@ -59,7 +59,8 @@ DECODE_SOURCES = ("kv_cache_eviction_03_amd/csrc/decode.hip",
 DECODE_TRAFFIC = {
     "opt-6.7b-layer-fp16": {"sha256": "be2177095510c15d554060f1d93eb213918d04261518bacd574c49931b7fd80c",
                             "read_bytes": 14174610, "write_bytes": 376832},
-    "llama-7b-stack-bf16": {"sha256": None, "read_bytes": None, "write_bytes": None},
+    "llama-7b-stack-bf16": {"sha256": "c5925dfe10cfc6691a4e85bfd49d4c59aecf65d14d62306b14788febfd22dc57",
+                            "read_bytes": 113028297, "write_bytes": 3015361},
 }
 
 
@@ -843,15 +844,19 @@ def opt67_layer(steps, warmup, seed=0, with_cold=True):
 HEADLINE_KERNEL = "decode_resident_kernel<__bf16,128,256,false,7>"
 
 
-def headline_stack(steps, warmup, seed=0, per_graph=64, cpu_units=64, cpu_seconds=10.0):
+def headline_stack(steps, warmup, seed=0, per_graph=64, cpu_units=64, decode_steps=None):
     """The LLaMA-7B-shaped stack end to end (see the module docstring). Returns the result
-    fields of the JSON line that describe the headline."""
+    fields of the JSON line that describe the headline. decode_steps (profiling runs only)
+    shortens the decode phase; every launch is still a cold launch of the same kernel on
+    the same layer shape, so per-dispatch counters are those of the full step."""
     import torch
 
     from kv_cache_eviction_03_amd import H2OStack
     from workloads import WORKLOADS, generate, sample_units
     dev = torch.device("cuda:0")
     w = WORKLOADS[3]
+    if decode_steps is not None:
+        w = w.scaled(steps=decode_steps)
     B, H, d, T, n, L = w.batch, w.heads, w.head_dim, w.prompt, w.steps, w.layers
     units = w.units_per_layer
     print(f"[bench] headline {w.name}: generating {L} layers' inputs", file=sys.stderr, flush=True)
@@ -991,6 +996,9 @@ def main():
                     help="model decode steps per captured graph of the headline")
     ap.add_argument("--headline-only", action="store_true",
                     help="only the headline step (no extras, no CPU baseline): for profiling")
+    ap.add_argument("--profile-decode-steps", type=int, default=None,
+                    help="profiling runs only: model decode steps of the headline step (the "
+                         "counter runs, which cannot hold 130k profiled dispatches)")
     ap.add_argument("--cpu-units", type=int, default=64,
                     help="sampled units the CPU oracle runs for cpu_baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -1065,9 +1073,12 @@ def main():
         return
 
     torch.cuda.set_device(0)
+    if args.profile_decode_steps is not None and not args.headline_only:
+        raise SystemExit("--profile-decode-steps is for --headline-only profiling runs")
     head, w, sample, total_units = headline_stack(args.steps, args.warmup, seed=args.seed,
                                                   per_graph=args.graph_steps,
-                                                  cpu_units=args.cpu_units)
+                                                  cpu_units=args.cpu_units,
+                                                  decode_steps=args.profile_decode_steps)
     result = {
         "metric": METRIC,
         "value": head["value"],
