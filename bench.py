@@ -336,7 +336,7 @@ def decode_cold(w, replicas=36, reps=5):
     caches = []
     for _ in range(replicas):
         c = H2OCache(w.batch, w.heads, w.head_dim, w.k_heavy, w.k_local, w.torch_dtype, dev,
-                     max_prompt=w.prompt)
+                     max_prompt=w.prompt, **w.cache_kw)
         c.reset()
         c.prefill(x["q_prompt"], x["k_prompt"], x["v_prompt"])
         caches.append(c)
@@ -355,8 +355,9 @@ def decode_cold(w, replicas=36, reps=5):
     byt = decode_bytes_per_unit(w) * w.units_per_layer
     del x, caches, out, g
     torch.cuda.empty_cache()
+    slots = "e4m3 slots" if w.slot_format == "e4m3" else f"{w.dtype} slots"
     return {"workload": f"{w.name} layer: B {w.batch}, H {w.heads}, d {w.head_dim}, {w.dtype}, "
-                        f"k = {w.k_heavy}+{w.k_local}",
+                        f"{slots}, k = {w.k_heavy}+{w.k_local}",
             "bound": "hbm", "kernel": "decode step, MALL-cold",
             "achieved": byt / (med * 1e-6) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": byt / (med * 1e-6) / 1e9 / HBM_PEAK_GBS,
@@ -493,13 +494,14 @@ def mfma_ceiling(reps=5, iters=4096):
                     f"v_mfma_f32_16x16x32_f16; median (and best) of {reps} launches"}
 
 
-def decode_cold_by_workload(ids_replicas=((3, 5), (4, 3), (5, 8))):
+def decode_cold_by_workload(ids_replicas=((3, 5), (4, 3), (5, 8)), slot_format="input"):
     """MALL-cold decode at the other workloads' layer shapes (cache filled by a k + 64 prompt,
-    so every step evicts)."""
+    so every step evicts); replicas sweep at least 512 MB per replay."""
     from workloads import WORKLOADS
     res = []
     for wid, r in ids_replicas:
-        w = WORKLOADS[wid].scaled(prompt=WORKLOADS[wid].k + 64, steps=1, layers=1)
+        w = WORKLOADS[wid].scaled(prompt=WORKLOADS[wid].k + 64, steps=1, layers=1,
+                                  slot_format=slot_format)
         d = decode_cold(w, replicas=r)
         res.append({k: d[k] for k in ("workload", "avg_launch_us", "best_launch_us", "achieved",
                                       "frac", "frac_at_min", "replicas", "state_swept_MB")})
@@ -1106,6 +1108,8 @@ def main():
             result["decode_by_workload_e4m3"] = decode_by_workload(slot_format="e4m3")
             if not args.no_cold:
                 result["decode_cold_by_workload"] = decode_cold_by_workload()
+                result["decode_cold_by_workload_e4m3"] = decode_cold_by_workload(
+                    ((3, 9), (4, 6), (5, 15)), slot_format="e4m3")
         if not args.no_ragged:
             result["ragged_step"] = ragged_step()
             result["decode_by_policy"] = decode_by_policy()
