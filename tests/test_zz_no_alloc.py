@@ -74,3 +74,75 @@ def test_noalloc_matches_the_workspace_entry_point():
     n_small = _run_pair(small)
     assert 0 < n_small < n_big <= H2O_NOALLOC_SCRATCH_BYTES
     assert _run_pair(resident) == 0
+
+
+def test_noalloc_under_graph_capture():
+    # The callers the allocation-free entry point is for include code under HIP graph capture:
+    # a graph of 48 h2o_decode_step_noalloc calls (split decode, k = 600), replayed from a
+    # saved state three times with eager work in between, must equal the workspace entry
+    # point's eager run every time.
+    import ctypes
+
+    from kv_cache_eviction_03_amd import H2OCache, h2o_decode_step
+    from kv_cache_eviction_03_amd._abi import check, library
+    w = Workload(49, "noalloc-graph-bf16", 1, 1, 2, 128, "bf16", 0, 648, 300, 300,
+                 heavy_frac=0.02)
+    n0, G = 600, 48                              # eager steps before the captured ones
+    announce(f"[noalloc] {w.name}: {G} captured steps after {n0} eager ones")
+    x = generate(w, seed=0, device="cuda")
+    B, H, d = w.batch, w.heads, w.head_dim
+    sb = x["q_dec"][0].numel() * x["q_dec"].element_size()
+    q0, k0, v0 = x["q_dec"].data_ptr(), x["k_dec"].data_ptr(), x["v_dec"].data_ptr()
+    lib = library()
+    names = ("k_slots", "v_slots", "slot_pos", "acc_score")
+
+    ref = H2OCache(B, H, d, w.k_heavy, w.k_local, w.torch_dtype, "cuda", **w.cache_kw)
+    ref.reset()
+    ref_out = torch.empty((G, B, H, d), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    for t in range(n0 + G):
+        o = ref_out[t - n0] if t >= n0 else torch.empty((B, H, d), dtype=torch.float32,
+                                                         device="cuda")
+        check(h2o_decode_step(ref.desc(), t, q0 + t * sb, k0 + t * sb, v0 + t * sb,
+                              o.data_ptr(), None, ref.workspace.data_ptr(),
+                              ref.workspace.numel(), stream), "decode")
+        if t == n0 - 1:
+            torch.cuda.synchronize()
+            snap = {nm: getattr(ref, nm).clone() for nm in names}
+    torch.cuda.synchronize()
+
+    c = H2OCache(B, H, d, w.k_heavy, w.k_local, w.torch_dtype, "cuda", **w.cache_kw)
+    for nm in names:
+        getattr(c, nm).copy_(snap[nm])
+    out = torch.empty((G, B, H, d), dtype=torch.float32, device="cuda")
+    desc = c.desc()
+    dref = ctypes.byref(desc)
+    # one eager call first, so the library takes the device address of its scratch outside
+    # the capture (the capture itself then allocates and queries nothing)
+    tmp = torch.empty((B, H, d), dtype=torch.float32, device="cuda")
+    probe = H2OCache(B, H, d, w.k_heavy, w.k_local, w.torch_dtype, "cuda", **w.cache_kw)
+    probe.reset()
+    check(lib.h2o_decode_step_noalloc(ctypes.byref(probe.desc()), 0, q0, k0, v0,
+                                      tmp.data_ptr(), None, stream), "noalloc probe")
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            s = torch.cuda.current_stream().cuda_stream
+            for i in range(G):
+                t = n0 + i
+                check(lib.h2o_decode_step_noalloc(dref, t, q0 + t * sb, k0 + t * sb,
+                                                  v0 + t * sb, out[i].data_ptr(), None, s),
+                      "captured noalloc decode")
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for nm in names:                             # eager work between the replays
+            getattr(c, nm).copy_(snap[nm])
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out), rep
+        for nm in names:
+            assert torch.equal(getattr(c, nm), getattr(ref, nm)), (rep, nm)
