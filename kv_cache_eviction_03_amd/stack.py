@@ -55,11 +55,13 @@ class H2OStack:
 
     def decode_step(self, dec, i: int, outs, aux=None) -> None:
         """Model step i: layer l decodes dec[l] = (q, k, v) [n, B, H, d] row i into outs[l]
-        ([B, H, d] fp32); aux[l], if given, is (victim_slot, evicted_pos, evicted_acc),
-        each [n, B, H] or None, written at row i."""
+        (fp32, [B, H, d], or [n, B, H, d] to keep every step's output at row i); aux[l], if
+        given, is (victim_slot, evicted_pos, evicted_acc), each [n, B, H] or None, written
+        at row i."""
         for l, (c, (q, k, v)) in enumerate(zip(self.caches, dec)):
             a = (None, None, None) if aux is None or aux[l] is None else aux[l]
-            c.decode(q[i], k[i], v[i], out=outs[l],
+            o = outs[l][i] if outs[l].dim() == 4 else outs[l]
+            c.decode(q[i], k[i], v[i], out=o,
                      victim_slot=None if a[0] is None else a[0][i],
                      evicted_pos=None if a[1] is None else a[1][i],
                      evicted_acc=None if a[2] is None else a[2][i])
