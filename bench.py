@@ -408,7 +408,59 @@ def _probe_lib():
     lib.mfma_probe.restype = ctypes.c_int
     lib.mfma_probe_flops.argtypes = [ctypes.c_int, ctypes.c_int]
     lib.mfma_probe_flops.restype = ctypes.c_double
+    lib.lds_bank_probe.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.c_void_p, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.lds_bank_probe.restype = ctypes.c_int
     return lib
+
+
+def _lds_patterns():
+    """(name, mode, 64 per-lane byte offsets or -1) for the LDS probe; mode 0 ds_read_b128,
+    1 ds_write_b64, 2 ds_read_b64, 3 ds_read_b64_tr_b16."""
+    L = range(64)
+
+    def pair(a, b, addr_b=256):
+        o = [-1] * 64
+        o[a], o[b] = 0, addr_b
+        return o
+    pats = [("b128 read, lane*16", 0, [l * 16 for l in L]),
+            ("b128 read, lane*256 (one bank quad)", 0, [l * 256 for l in L]),
+            ("b128 read, prefill K operand (16 rows of 256 B, chunk ^ row)", 0,
+             [(l % 16) * 256 + (((l // 16) ^ (l % 16)) & 15) * 16 for l in L])]
+    for x in (128, 192, 256, 272, 4096):
+        pats.append((f"b128 read, lane 0 at 0 and lane 1 at {x}", 0, pair(0, 1, x)))
+    for k in (2, 3, 4, 8, 12, 15, 16, 20, 24, 28, 32):
+        pats.append((f"b128 read, lane 0 at 0 and lane {k} at 256", 0, pair(0, k)))
+    pats += [("b64 write, lane*8", 1, [l * 8 for l in L]),
+             ("b64 write, lane*256", 1, [l * 256 for l in L])]
+    for x in (64, 128):
+        pats.append((f"b64 write, lane 0 at 0 and lane 1 at {x}", 1, pair(0, 1, x)))
+    for k in (8, 15, 16, 31, 32):
+        pats.append((f"b64 write, lane 0 at 0 and lane {k} at 256", 1, pair(0, k)))
+    pats += [("b64 read, lane*8", 2, [l * 8 for l in L]),
+             ("b64 transposing read, lane*8", 3, [l * 8 for l in L])]
+    return pats
+
+
+def lds_probe(iters=100):
+    """One dispatch per pattern of _lds_patterns(), in order (the LDS cycle and conflict
+    counters come from rocprofv3 --pmc)."""
+    import ctypes
+    import torch
+    lib = _probe_lib()
+    offs_dev = torch.empty(64, dtype=torch.int32, device="cuda")
+    sink = torch.empty(256, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    rows = []
+    for name, mode, offs in _lds_patterns():
+        arr = (ctypes.c_int * 64)(*offs)
+        rc = lib.lds_bank_probe(arr, offs_dev.data_ptr(), mode, iters, sink.data_ptr(), stream)
+        if rc != 0:
+            raise RuntimeError(f"lds_bank_probe({name!r}) failed: {rc}")
+        torch.cuda.synchronize()
+        rows.append({"lds_pattern": name, "mode": mode, "wave_instructions": 4 * 4 * iters,
+                     "active_lanes": sum(o >= 0 for o in offs)})
+    return rows
 
 
 # Whole 32 KB tiles per workgroup, nontemporal loads, 512 workgroups: the fastest of the
@@ -1028,10 +1080,12 @@ def main():
                     help="only the HBM and MFMA probes; print their figures")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 512 MiB device copy (calibrates HBM byte counters)")
+    ap.add_argument("--lds-probe", action="store_true",
+                    help="only run the LDS access-pattern probe (one dispatch per pattern)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: the H2O path has no cross-GPU exchange and this "
-              "build runs on a single MI355X; run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the H2O path has no cross-GPU exchange; "
+              "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -1044,6 +1098,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 3}))
+        return
+    if args.lds_probe:
+        for r in lds_probe():
+            print(json.dumps(r), flush=True)
         return
     if args.decode_shapes:
         for r in decode_by_workload():
