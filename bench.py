@@ -206,7 +206,7 @@ def decode_by_policy(n=32, reps=5):
     return res
 
 
-def decode_by_workload(ids=(2, 3, 4, 5), n=32, reps=5, slot_format="input"):
+def decode_by_workload(ids=(2, 3, 4, 5), n=64, reps=5, slot_format="input"):
     """Decode launches of each workload's layer shape, graph-replayed, timed with HIP events.
 
     The cache is filled by a prefill of k + 64 tokens (so every step evicts), then n
@@ -318,14 +318,16 @@ def ragged_step(reps=20, seed=7):
     return res
 
 
-def decode_cold(w, replicas=36, reps=5):
+def decode_cold(w, replicas=36, reps=5, min_launches=64):
     """A workload's decode step with the Infinity Cache (MALL) out of play.
 
-    `replicas` independent caches, each prefilled from the same prompt, are visited in turn
-    by one graph of `replicas` decode steps, so consecutive steps touch disjoint slot arrays
-    and the state swept per replay (replicas x the step's bytes, >= 512 MB) is at least twice
-    the 256 MB MALL. The same launch shape as the warm figure; median and best replay, per
-    step. Replays repeat each replica's position t; that leaves the work per step unchanged.
+    `replicas` independent caches, each prefilled from the same prompt, are visited in turn,
+    round after round, by one graph of at least `min_launches` decode steps, so consecutive
+    steps touch disjoint slot arrays and between two visits of one replica the others sweep
+    (replicas - 1) x the step's bytes, more than the 256 MB MALL. Enough launches per graph
+    that the replay's own start-up cost is spread as thinly as in a model's decode graph.
+    The same launch shape as the warm figure; median and best replay, per step. Each visit
+    repeats its replica's position t; that leaves the work per step unchanged.
     """
     import torch
 
@@ -344,14 +346,16 @@ def decode_cold(w, replicas=36, reps=5):
     torch.cuda.synchronize()
     side = torch.cuda.Stream(dev)
     g = torch.cuda.CUDAGraph()
+    rounds = -(-min_launches // replicas)
     with torch.cuda.stream(side):
         with torch.cuda.graph(g, stream=side):
-            for c in caches:
-                c.decode(x["q_dec"][0], x["k_dec"][0], x["v_dec"][0], out=out)
+            for _ in range(rounds):
+                for c in caches:
+                    c.decode(x["q_dec"][0], x["k_dec"][0], x["v_dec"][0], out=out)
     torch.cuda.synchronize()
     g.replay()
     torch.cuda.synchronize()
-    med, best = stats(replay_times(g, reps, replicas))
+    med, best = stats(replay_times(g, reps, rounds * replicas))
     byt = decode_bytes_per_unit(w) * w.units_per_layer
     del x, caches, out, g
     torch.cuda.empty_cache()
@@ -364,8 +368,10 @@ def decode_cold(w, replicas=36, reps=5):
             "frac_at_min": byt / (best * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "avg_launch_us": med, "best_launch_us": best,
             "algorithmic_bytes_per_launch": byt, "replicas": replicas,
-            "state_swept_MB": replicas * byt / 1e6,
-            "duration_from": "HIP events around graph replays of one launch per replica (median)"}
+            "launches_per_replay": rounds * replicas,
+            "swept_between_visits_MB": (replicas - 1) * byt / 1e6,
+            "duration_from": "HIP events around graph replays of every replica in turn, round "
+                             "after round (median replay over its launches)"}
 
 
 def launch_floor(w, n=32, reps=10):
@@ -546,9 +552,9 @@ def mfma_ceiling(reps=5, iters=4096):
                     f"v_mfma_f32_16x16x32_f16; median (and best) of {reps} launches"}
 
 
-def decode_cold_by_workload(ids_replicas=((3, 5), (4, 3), (5, 8)), slot_format="input"):
+def decode_cold_by_workload(ids_replicas=((3, 5), (4, 4), (5, 8)), slot_format="input"):
     """MALL-cold decode at the other workloads' layer shapes (cache filled by a k + 64 prompt,
-    so every step evicts); replicas sweep at least 512 MB per replay."""
+    so every step evicts); between two visits of a replica the others sweep >= 356 MB."""
     from workloads import WORKLOADS
     res = []
     for wid, r in ids_replicas:
@@ -556,7 +562,8 @@ def decode_cold_by_workload(ids_replicas=((3, 5), (4, 3), (5, 8)), slot_format="
                                   slot_format=slot_format)
         d = decode_cold(w, replicas=r)
         res.append({k: d[k] for k in ("workload", "avg_launch_us", "best_launch_us", "achieved",
-                                      "frac", "frac_at_min", "replicas", "state_swept_MB")})
+                                      "frac", "frac_at_min", "replicas", "launches_per_replay",
+                                      "swept_between_visits_MB")})
     return res
 
 
