@@ -291,7 +291,9 @@ h2o_status h2o_decode_step_ragged(const h2o_cache_desc* cache, const int32_t* t,
  * current device (else H2O_ERR_INVALID). Every call on one GPU shares that
  * GPU's array (its contents on entry never matter), so calls that can overlap
  * on one GPU — on different streams, or from different threads — race and
- * give undefined results; order them on one stream.
+ * give undefined results; order them on one stream. The first call on a GPU
+ * looks up the array's device address (hipGetSymbolAddress); a caller that
+ * records the calls in a HIP graph makes one call outside the capture first.
  */
 #define H2O_NOALLOC_SCRATCH_BYTES (8u << 20)
 h2o_status h2o_decode_step_noalloc(const h2o_cache_desc* cache, int64_t t, const void* q,
