@@ -57,10 +57,10 @@ METRIC = "H2O decode tokens/s at 20% KV budget + % of HBM roofline (prefill % MF
 DECODE_SOURCES = ("kv_cache_eviction_03_amd/csrc/decode.hip",
                   "kv_cache_eviction_03_amd/csrc/h2o_device.hpp")
 DECODE_TRAFFIC = {
-    "opt-6.7b-layer-fp16": {"sha256": "be2177095510c15d554060f1d93eb213918d04261518bacd574c49931b7fd80c",
-                            "read_bytes": 14174610, "write_bytes": 376832},
-    "llama-7b-stack-bf16": {"sha256": "c5925dfe10cfc6691a4e85bfd49d4c59aecf65d14d62306b14788febfd22dc57",
-                            "read_bytes": 113028297, "write_bytes": 3015361},
+    "opt-6.7b-layer-fp16": {"sha256": "615154c49d7d9cd9dfa157b1f414c8e799d8d26fb816012a74968ab1b95558f2",
+                            "read_bytes": 14175042, "write_bytes": 376832},
+    "llama-7b-stack-bf16": {"sha256": "615154c49d7d9cd9dfa157b1f414c8e799d8d26fb816012a74968ab1b95558f2",
+                            "read_bytes": 113017950, "write_bytes": 3015344},
 }
 
 

@@ -158,6 +158,12 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint2 ld8(const void* p) { return *reinterpret_cast<const uint2*>(p); }
+// Nontemporal 8-byte load (E4M3 slot rows: read once per step, like ld16_nt).
+__device__ __forceinline__ uint2 ld8_nt(const void* p) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return make_uint2(x[0], x[1]);
+}
 __device__ __forceinline__ void st8(void* p, const uint2& v) { *reinterpret_cast<uint2*>(p) = v; }
 
 // One 16-byte chunk of T (8 elements) -> its 8 codes: each element times `inv` (one fp32
@@ -204,7 +210,9 @@ template <typename T> struct SlotChunk<T, true> {
   static_assert(sizeof(T) == 2, "E4M3 slots take fp16 or bf16 inputs");
   typedef uint2 type;
   typedef uint8_t elem;
-  __device__ static type load(const elem* p) { return ld8(p); }
+  // Slot rows are loaded nontemporal, as the 16-bit decode kernels load theirs: a step
+  // reads each once, and a deep model visits every other layer before it comes back.
+  __device__ static type load(const elem* p) { return ld8_nt(p); }
   __device__ static void store(elem* p, const type& v) { st8(p, v); }
 };
 
