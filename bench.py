@@ -417,6 +417,9 @@ def _probe_lib():
     lib.lds_bank_probe.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.c_void_p, ctypes.c_int,
                                    ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     lib.lds_bank_probe.restype = ctypes.c_int
+    lib.issue_overlap_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.issue_overlap_probe.restype = ctypes.c_int
     return lib
 
 
@@ -446,6 +449,46 @@ def _lds_patterns():
     pats += [("b64 read, lane*8", 2, [l * 8 for l in L]),
              ("b64 transposing read, lane*8", 3, [l * 8 for l in L])]
     return pats
+
+
+OVERLAP_MODES = {
+    0: "16 MFMA 16x16x32",
+    1: "16 v_exp_f32",
+    2: "16 MFMA + 16 v_exp_f32, interleaved",
+    3: "16 MFMA, then 16 v_exp_f32",
+    4: "waves 0-3: 16 v_exp_f32; waves 4-7: 16 MFMA",
+    5: "16 v_fma_f32",
+    6: "16 MFMA + 16 v_fma_f32, interleaved",
+    7: "8 MFMA 32x32x16",
+    8: "8 MFMA 32x32x16 + 16 v_exp_f32, interleaved",
+}
+
+
+def overlap_probe(iters=2000, blocks=256):
+    """s_memtime ticks per iteration of each instruction mix of the issue-overlap probe, one
+    workgroup per CU, with one and with two waves per SIMD; waves 0-3 and 4-7 of a
+    workgroup are averaged apart (a SIMD's older wave issues first)."""
+    import torch
+    lib = _probe_lib()
+    sink = torch.empty(blocks * 512, dtype=torch.float32, device="cuda")
+    ticks = torch.zeros(blocks * 8, dtype=torch.int64, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    rows = []
+    for wps in (1, 2):
+        for mode, name in OVERLAP_MODES.items():
+            ticks.zero_()
+            rc = lib.issue_overlap_probe(mode, wps, blocks, iters, sink.data_ptr(),
+                                         ticks.data_ptr(), stream)
+            if rc != 0:
+                raise RuntimeError(f"issue_overlap_probe(mode {mode}) failed: {rc}")
+            torch.cuda.synchronize()
+            t = ticks[:blocks * 4 * wps].view(blocks, 4 * wps).double() / iters   # one per wave
+            row = {"mix": name, "mode": mode, "waves_per_simd": wps,
+                   "ticks_waves_0_3": round(float(t[:, :4].mean()), 1)}
+            if wps == 2:
+                row["ticks_waves_4_7"] = round(float(t[:, 4:].mean()), 1)
+            rows.append(row)
+    return rows
 
 
 def lds_probe(iters=100):
@@ -1089,6 +1132,8 @@ def main():
                     help="only run a plain 512 MiB device copy (calibrates HBM byte counters)")
     ap.add_argument("--lds-probe", action="store_true",
                     help="only run the LDS access-pattern probe (one dispatch per pattern)")
+    ap.add_argument("--overlap-probe", action="store_true",
+                    help="only run the MFMA / vector ALU issue-overlap probe")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the H2O path has no cross-GPU exchange; "
@@ -1108,6 +1153,10 @@ def main():
         return
     if args.lds_probe:
         for r in lds_probe():
+            print(json.dumps(r), flush=True)
+        return
+    if args.overlap_probe:
+        for r in overlap_probe():
             print(json.dumps(r), flush=True)
         return
     if args.decode_shapes:

@@ -18,7 +18,8 @@ def lib():
 
 
 def test_probe_library_exports(lib):
-    for name in ("hbm_read_probe", "mfma_probe", "mfma_probe_flops", "lds_bank_probe"):
+    for name in ("hbm_read_probe", "mfma_probe", "mfma_probe_flops", "lds_bank_probe",
+                 "issue_overlap_probe"):
         assert hasattr(lib, name), name
 
 
@@ -44,3 +45,11 @@ def test_lds_patterns_are_in_bounds():
         assert len(offs) == 64, name
         assert all(o == -1 or (0 <= o and o % size == 0 and o + size <= 65536) for o in offs), name
         assert any(o >= 0 for o in offs), name
+
+
+def test_overlap_probe_rejects_bad_arguments_before_any_gpu_call(lib):
+    # mode, waves per SIMD, workgroups, iterations: each out of range returns -1 unlaunched
+    for args in ((-1, 1, 256, 10), (len(bench.OVERLAP_MODES), 1, 256, 10), (0, 0, 256, 10),
+                 (0, 3, 256, 10), (0, 1, 0, 10), (0, 1, 256, 0)):
+        assert lib.issue_overlap_probe(*args, None, None, None) == -1, args
+    assert sorted(bench.OVERLAP_MODES) == list(range(len(bench.OVERLAP_MODES)))
