@@ -564,6 +564,50 @@ def hbm_ceiling(reps=10):
     return out
 
 
+def read_at_launch_size(nbytes=115_294_208, regions=32, per_replay=64, reps=5):
+    """The streaming-read probe at one decode launch's size (default: the LLaMA-7B-shaped
+    layer's 115.3 MB), launched as the stack's decode launches are: back to back in a HIP
+    graph, each launch reading one of `regions` distinct regions, so that a region has
+    been swept out of the MALL when it is read again. Tried at 1, 2, 4 and 8 passes of
+    whole 32 KB tiles per workgroup; the per-launch time includes the launch's start-up
+    and tail, the cost any kernel of this size pays."""
+    import torch
+    lib = _probe_lib()
+    tile = 16 * 8 * 256                          # bytes per workgroup per pass
+    rows = []
+    for passes in (1, 2, 4, 8):
+        blocks = max(1, round(nbytes / (passes * tile)))
+        size = blocks * passes * tile
+        buf = torch.ones(regions * size // 4, dtype=torch.float32, device="cuda:0")
+        sink = torch.empty(blocks * 256, dtype=torch.int32, device="cuda:0")
+
+        def launch(i):
+            base = buf.data_ptr() + (i % regions) * size
+            if lib.hbm_read_probe(base, size, sink.data_ptr(), blocks, PROBE_LAYOUT,
+                                  torch.cuda.current_stream().cuda_stream):
+                raise RuntimeError("hbm_read_probe refused its sizes or failed to launch")
+        for i in range(regions):
+            launch(i)
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream("cuda:0")
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side), torch.cuda.graph(g, stream=side):
+            for i in range(per_replay):
+                launch(i)
+        torch.cuda.synchronize()
+        med, mn = stats(replay_times(g, reps, per_replay))
+        rows.append({"workgroups": blocks, "passes": passes, "bytes_per_launch": size,
+                     "us_per_launch": med, "us_per_launch_min": mn,
+                     "GBps": size / med / 1e3, "frac_of_nominal": size / med / 1e3 / HBM_PEAK_GBS})
+        del g, buf, sink
+        torch.cuda.empty_cache()
+    best = min(rows, key=lambda r: r["us_per_launch"] * nbytes / r["bytes_per_launch"])
+    return {"best_GBps": best["GBps"], "best_frac_of_nominal": best["frac_of_nominal"],
+            "best_us_at_bytes": best["us_per_launch"] * nbytes / best["bytes_per_launch"],
+            "bytes": nbytes, "regions": regions, "launches_per_replay": per_replay,
+            "by_shape": rows}
+
+
 def mfma_ceiling(reps=5, iters=4096):
     """The dense fp16 MFMA rate of a register-only loop (libh2o_probes.so: eight
     independent 16x16x32 accumulation chains per wave, 256-thread workgroups, 8 per CU)."""
@@ -1185,7 +1229,8 @@ def main():
         print(json.dumps(prefill_mfma_probe()), flush=True)
         return
     if args.ceilings_only:
-        print(json.dumps({"hbm": hbm_ceiling(), "mfma": mfma_ceiling()}), flush=True)
+        print(json.dumps({"hbm": hbm_ceiling(), "mfma": mfma_ceiling(),
+                          "hbm_read_at_decode_launch_size": read_at_launch_size()}), flush=True)
         return
 
     torch.cuda.set_device(0)
@@ -1216,6 +1261,7 @@ def main():
         if not args.no_mfma_probe:
             result["prefill_mfma_opt30b"] = prefill_mfma_probe()
         result["hbm_measured_ceiling"] = hbm_ceiling()
+        result["hbm_read_at_decode_launch_size"] = read_at_launch_size()
         result["mfma_measured_ceiling"] = mfma_ceiling()
         if not args.no_decode_shapes:
             result["decode_by_workload"] = decode_by_workload()
