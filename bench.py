@@ -957,7 +957,7 @@ def opt67_layer(steps, warmup, seed=0, with_cold=True):
            "decode_launch_us": dec_us, "decode_launch_us_min": dec_us_min,
            "decode_tokens_per_s": B / (dec_us * 1e-6),
            "roofline_warm": {"bound": "hbm",
-                             "kernel": "decode_resident_kernel<_Float16,128,256,false,7>",
+                             "kernel": "decode_resident_kernel<_Float16,128,256,false,7,false>",
                              "achieved": dec_bytes / (dec_us * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
                              "unit": "GB/s",
                              "frac": dec_bytes / (dec_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
@@ -981,7 +981,7 @@ def opt67_layer(steps, warmup, seed=0, with_cold=True):
     torch.cuda.empty_cache()
     if with_cold:
         res["roofline_cold"] = decode_cold(w)
-        res["roofline_cold"]["kernel"] = ("decode_resident_kernel<_Float16,128,256,false,7>, "
+        res["roofline_cold"]["kernel"] = ("decode_resident_kernel<_Float16,128,256,false,7,false>, "
                                           "MALL-cold")
         dense = dense_comparator(w)
         dense["h2o_decode_speedup"] = dense["decode_us_per_step"] / dec_us
@@ -989,7 +989,7 @@ def opt67_layer(steps, warmup, seed=0, with_cold=True):
     return res
 
 
-HEADLINE_KERNEL = "decode_resident_kernel<__bf16,128,256,false,7>"
+HEADLINE_KERNEL = "decode_resident_kernel<__bf16,128,256,false,7,true>"
 
 
 def headline_stack(steps, warmup, seed=0, per_graph=64, cpu_units=64, decode_steps=None):
