@@ -566,7 +566,7 @@ def hbm_ceiling(reps=10):
 
 def read_at_launch_size(nbytes=115_294_208, regions=32, per_replay=64, reps=5):
     """The streaming-read probe at one decode launch's size (default: the LLaMA-7B-shaped
-    layer's 115.3 MB), launched as the stack's decode launches are: back to back in a HIP
+    layer's 115.3 MB; the OPT-6.7B-shaped layer's is 14.4 MB), launched as the stack's decode launches are: back to back in a HIP
     graph, each launch reading one of `regions` distinct regions, so that a region has
     been swept out of the MALL when it is read again. Tried at 1, 2, 4 and 8 passes of
     whole 32 KB tiles per workgroup; the per-launch time includes the launch's start-up
@@ -1230,7 +1230,9 @@ def main():
         return
     if args.ceilings_only:
         print(json.dumps({"hbm": hbm_ceiling(), "mfma": mfma_ceiling(),
-                          "hbm_read_at_decode_launch_size": read_at_launch_size()}), flush=True)
+                          "hbm_read_at_decode_launch_size": read_at_launch_size(),
+                          "hbm_read_at_opt67_launch_size": read_at_launch_size(
+                              nbytes=14_411_776, regions=36)}), flush=True)
         return
 
     torch.cuda.set_device(0)
@@ -1262,6 +1264,8 @@ def main():
             result["prefill_mfma_opt30b"] = prefill_mfma_probe()
         result["hbm_measured_ceiling"] = hbm_ceiling()
         result["hbm_read_at_decode_launch_size"] = read_at_launch_size()
+        result["hbm_read_at_opt67_launch_size"] = read_at_launch_size(nbytes=14_411_776,
+                                                                      regions=36)
         result["mfma_measured_ceiling"] = mfma_ceiling()
         if not args.no_decode_shapes:
             result["decode_by_workload"] = decode_by_workload()
