@@ -404,6 +404,28 @@ def test_stream_late_window_from_gpu_snapshot():
     torch.cuda.empty_cache()
 
 
+def test_fp32_long_prompts_with_sink_keys():
+    # fp32 inputs, prompts of 1029 and up to 1218 keys with four sink keys each: over that
+    # many keys, with a few dominating, an fp32 running sum of the prefill's softmax drifts
+    # past the 1e-5 output bound (1.3e-5 and 1.7e-5 were seen on these two cases); the
+    # fp64 running sum holds it. One padded case and one ragged batch, both every unit.
+    from tests.parity import run_gpu_ragged
+    w = Workload(1211, "f32-long-sinks", 1, 1, 1, 64, "f32", 1029, 37, 294, 57, sinks=4,
+                 policy="sinks", policy_param=0)
+    announce(f"[parity] {w.name}: T={w.prompt} d={w.head_dim} k={w.k_heavy}+{w.k_local}")
+    x = generate(w, seed=11, device="cuda")
+    r = run_gpu(w, x)
+    agg = check_units(w, x, r, range(w.units_per_layer))
+    announce(f"[parity] {w.name}: prefill {agg['prefill_out']:.2e} decode {agg['decode_out']:.2e}")
+    w = Workload(201, "f32-long-ragged", 3, 1, 2, 128, "f32", 1218, 42, 973, 60, sinks=4)
+    lens = [1218, 1045, 708]
+    announce(f"[parity] {w.name}: lens={lens} d={w.head_dim} k={w.k_heavy}+{w.k_local}")
+    x = generate(w, seed=12, device="cuda")
+    r = run_gpu_ragged(w, x, lens)
+    agg = check_units(w, x, r, range(w.units_per_layer), lens=lens)
+    announce(f"[parity] {w.name}: prefill {agg['prefill_out']:.2e} decode {agg['decode_out']:.2e}")
+
+
 def test_prefill_exact_ties_keep_the_newest():
     # Dead keys point against every query, so their column sums underflow to exactly 0
     # on both sides; k_heavy exceeds the live candidates, so the heavy cutoff falls
