@@ -57,10 +57,10 @@ METRIC = "H2O decode tokens/s at 20% KV budget + % of HBM roofline (prefill % MF
 DECODE_SOURCES = ("kv_cache_eviction_03_amd/csrc/decode.hip",
                   "kv_cache_eviction_03_amd/csrc/h2o_device.hpp")
 DECODE_TRAFFIC = {
-    "opt-6.7b-layer-fp16": {"sha256": "615154c49d7d9cd9dfa157b1f414c8e799d8d26fb816012a74968ab1b95558f2",
-                            "read_bytes": 14175042, "write_bytes": 376832},
-    "llama-7b-stack-bf16": {"sha256": "615154c49d7d9cd9dfa157b1f414c8e799d8d26fb816012a74968ab1b95558f2",
-                            "read_bytes": 113017950, "write_bytes": 3015344},
+    "opt-6.7b-layer-fp16": {"sha256": "de7371b7c721b04aad81faa9b121d08086a29622151b90a241cab0d0bed55183",
+                            "read_bytes": 14170156, "write_bytes": 376832},
+    "llama-7b-stack-bf16": {"sha256": "de7371b7c721b04aad81faa9b121d08086a29622151b90a241cab0d0bed55183",
+                            "read_bytes": 113014501, "write_bytes": 3015298},
 }
 
 

@@ -211,6 +211,12 @@ __device__ __forceinline__ uint64_t score_key(float a, int pos) {
 
 // ------------------------------------------------------------------ resident --
 
+// Workgroup barrier that orders LDS only: vector memory operations in flight stay in flight
+// (a __syncthreads first waits for every outstanding load and store of the wave).
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Component-wise select of 16-byte chunks (a select of whole vectors can be lowered
 // through private memory).
 __device__ __forceinline__ uint4 sel16(bool c, const uint4& a, const uint4& b) {
@@ -222,6 +228,8 @@ template <typename T, int D, int THREADS, bool F8, int UB = kBatch, bool TP = fa
 // before the V rows are loaded into the same registers, and the new token's row reaches
 // the store through LDS, so a lane holds one set of slot chunks instead of two (at most 64
 // VGPRs: eight waves per SIMD, the LLaMA-7B layer's 2048 workgroups all resident at once).
+// With 256 threads, the scores, the argmin and the bookkeeping stores are done while the
+// V rows are in flight, so that only the PV product, one fold and the stores follow them.
 // UB slots per row group: kBatch, or 7 for 16-bit inputs when k + 1 <= 7 row groups' worth
 // (the k = 104 caches of the OPT-6.7B and LLaMA-7B layers need 105 of the 112 slots; the
 // OPT-30B layer's 411 need 7 of 8 at 1024 threads): one load and one logit fewer per lane.
@@ -304,6 +312,91 @@ void decode_resident_kernel(DecodeParams p) {
     vst = vnr;
   }
   float s[U], mg, lg, o[VEC];
+
+  // Once every row group's maximum, sum and logits are in LDS. fold(): the row groups'
+  // scale factors 2^(m_g - M), formed by every wave for itself with wave-uniform folds
+  // (lane r holds groups r and r + 64, one exp2 per lane) into the wave's own LDS copy, and
+  // the normaliser. choose(): every slot's new score, the masked argmin and the bookkeeping
+  // stores; it gives the victim's slot to the lanes that store its row. Neither needs a V
+  // row.
+  struct Fold {
+    float M, inv, p_new, lg_own;
+  };
+  auto fold = [&]() -> Fold {
+    static_assert(ROWS <= 2 * kWave, "at most two row groups per lane");
+    // Every LDS read of this stretch is issued here (clamped indices), one round trip.
+    const bool in_a = lane < ROWS, in_b = lane + kWave < ROWS;
+    const float m_a0 = s_m[in_a ? lane : 0], m_b0 = s_m[in_b ? lane + kWave : 0];
+    const float l_a0 = s_l[in_a ? lane : 0], l_b0 = s_l[in_b ? lane + kWave : 0];
+    const float lg_new = s_logit[n], lg_own = s_logit[own ? jo : 0];
+    const float m_a = in_a ? m_a0 : -INFINITY;
+    const float m_b = in_b ? m_b0 : -INFINITY;
+    const float M = wave_max_uniform(fmaxf(m_a, m_b));
+    const float sc_a = m_a == -INFINITY ? 0.f : fast_exp2(m_a - M);
+    const float sc_b = m_b == -INFINITY ? 0.f : fast_exp2(m_b - M);
+    const float l_ab = (in_a ? l_a0 * sc_a : 0.f) + (in_b ? l_b0 * sc_b : 0.f);
+    const float inv = __builtin_amdgcn_rcpf(wave_sum_uniform(l_ab));
+    if (lane < ROWS) s_scw[wave][lane] = sc_a;
+    if (lane + kWave < ROWS) s_scw[wave][lane + kWave] = sc_b;
+    return {M, inv, fast_exp2(lg_new - M) * inv, lg_own};
+  };
+  auto choose = [&](const Fold& f) -> int {
+    uint64_t key = ~0ull;
+    float a = 0.f;
+    if (own) {
+      const float pj = fast_exp2(f.lg_own - f.M) * f.inv;
+      a = acc_old + pj;
+      acc[jo] = a;
+      if (full && pos_old <= limit)
+        key = score_key(policy_key(p.policy, p.policy_param, a, pj, pos_old), pos_old);
+    }
+    const uint64_t wmin = wave_min_u64_uniform(key);
+    if (lane == 0) s_key[wave] = wmin;
+    // The waves' minima. Taken while V rows are in flight (two phases, 256 threads) this
+    // barrier must not wait for them; elsewhere a __syncthreads measured slightly faster.
+    if constexpr (TP && THREADS == 256) lds_barrier();
+    else __syncthreads();
+    uint64_t best = s_key[0];
+#pragma unroll
+    for (int w = 1; w < S::WAVES; ++w) best = s_key[w] < best ? s_key[w] : best;
+
+    int dst = -1;
+    bool meta = false;
+    if (full) {
+      const uint64_t hit = __ballot(key == best && best != ~0ull);
+      const uint64_t grp = (hit >> ((lane / LANES) * LANES)) & ((1ull << LANES) - 1ull);
+      if (grp) dst = (__ffsll((unsigned long long)grp) - 1) * ROWS + g;
+      meta = key == best && best != ~0ull;
+    } else {
+      if (g == n % ROWS) dst = n;
+      meta = jo == n;
+    }
+    if (meta) {                                 // the lane that wrote acc[dst] above, if any
+      pos[dst] = t;
+      acc[dst] = f.p_new;
+      if (p.victim_slot) p.victim_slot[unit] = full ? dst : -1;
+      if (p.evicted_pos) p.evicted_pos[unit] = full ? pos_old : -1;
+      if (p.evicted_acc) p.evicted_acc[unit] = full ? a : 0.f;
+    }
+    return dst;
+  };
+  // Output, once s_red holds every row group's partial: every wave takes CW columns; the
+  // SL lanes of one column (lanes c, c + CW, ...) each sum RS of the row groups, then fold
+  // their partial sums with lane swaps.
+  auto write_out = [&](float scale) {
+    constexpr int SL = THREADS / D, CW = kWave / SL, RS = ROWS / SL;
+    static_assert(SL * CW == kWave && RS * SL == ROWS, "output split");
+    const int c = wave * CW + lane % CW, sl = lane / CW;
+    float v = 0.f;
+#pragma unroll
+    for (int j = 0; j < RS; ++j) {
+      const int r = sl * RS + j;
+      v = fmaf(s_red[r * D + c], s_scw[wave][r], v);
+    }
+#pragma unroll
+    for (int w = CW; w < kWave; w *= 2) v += __shfl_xor(v, w, kWave);
+    if (sl == 0) p.out[(size_t)unit * D + c] = v * scale;
+  };
   if constexpr (TP) {
     // Row n (the new token) sits in row group n % ROWS at u = n / ROWS (k + 1 <= U * ROWS).
     const int un = n / ROWS;
@@ -337,22 +430,50 @@ void decode_resident_kernel(DecodeParams p) {
       s[u] = fast_exp2(s[u] - mref);
       lg += s[u];
     }
+    // The V rows of the slots, weighted, and the new token's V row (for the store).
+    auto weigh_v = [&]() {
 #pragma unroll
-    for (int i = 0; i < VEC; ++i) o[i] = 0.f;
+      for (int i = 0; i < VEC; ++i) o[i] = 0.f;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float vf[VEC];
-      unpack(vr[u], vf, T{});
+      for (int u = 0; u < U; ++u) {
+        float vf[VEC];
+        unpack(vr[u], vf, T{});
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) o[i] = fmaf(s[u], vf[i], o[i]);
+        for (int i = 0; i < VEC; ++i) o[i] = fmaf(s[u], vf[i], o[i]);
+      }
+      __builtin_amdgcn_sched_barrier(0);          // the copy below waits for every V row
+      if (gn) {
+        uint4 x = vr[0];
+#pragma unroll
+        for (int u = 1; u < U; ++u) x = sel16(u == un, vr[u], x);
+        s_new[1][rl] = x;
+      }
+    };
+    if constexpr (THREADS == 256) {
+      // The decision needs only the logits, so it is taken while the V rows are in
+      // flight; once they land, the PV product, one fold and the stores remain. The
+      // barriers before that wait on LDS only: a __syncthreads would first wait for every
+      // load in flight. (The 1024-thread shape would need more than the 64 VGPRs that keep
+      // two of its workgroups on a CU; it decides after the V rows.)
+      if (rl == 0) {
+        s_m[g] = mg;
+        s_l[g] = lg;
+      }
+      lds_barrier();                            // group maxima, sums and logits staged
+      const Fold f = fold();
+      const int dst = choose(f);
+      weigh_v();
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) s_red[g * D + rl * VEC + i] = o[i];
+      __syncthreads();                          // every V read is consumed
+      write_out(f.inv);
+      if (dst >= 0) {
+        SC::store(ks + (size_t)dst * D + rl * VEC, s_new[0][rl]);
+        SC::store(vs + (size_t)dst * D + rl * VEC, s_new[1][rl]);
+      }
+      return;
     }
-    __builtin_amdgcn_sched_barrier(0);          // the copy below waits for every V row
-    if (gn) {
-      uint4 x = vr[0];
-#pragma unroll
-      for (int u = 1; u < U; ++u) x = sel16(u == un, vr[u], x);
-      s_new[1][rl] = x;
-    }
+    weigh_v();
   } else {
     group_softmax<T, D, U, THREADS>(qr, p.qk_scale, kr, vr, g, n, s, mg, lg, o);
   }
@@ -367,72 +488,10 @@ void decode_resident_kernel(DecodeParams p) {
       for (int u = 0; u < U; ++u) s_logit[u * ROWS + g] = s[u];
     }
   }
-  __syncthreads();                              // (1) every K/V read is consumed
-  // Scale factors 2^(m_g - M) of the row groups, formed by every wave for itself with
-  // wave-uniform folds (lane r holds group r and r + 64, one exp2 per lane) into the
-  // wave's own LDS copy, so no further barrier is needed.
-  static_assert(ROWS <= 2 * kWave, "at most two row groups per lane");
-  // Every LDS read of this stretch is issued here (clamped indices), one round trip.
-  const bool in_a = lane < ROWS, in_b = lane + kWave < ROWS;
-  const float m_a0 = s_m[in_a ? lane : 0], m_b0 = s_m[in_b ? lane + kWave : 0];
-  const float l_a0 = s_l[in_a ? lane : 0], l_b0 = s_l[in_b ? lane + kWave : 0];
-  const float lg_new = s_logit[n], lg_own = s_logit[own ? jo : 0];
-  const float m_a = in_a ? m_a0 : -INFINITY;
-  const float m_b = in_b ? m_b0 : -INFINITY;
-  const float M = wave_max_uniform(fmaxf(m_a, m_b));
-  const float sc_a = m_a == -INFINITY ? 0.f : fast_exp2(m_a - M);
-  const float sc_b = m_b == -INFINITY ? 0.f : fast_exp2(m_b - M);
-  const float l_ab = (in_a ? l_a0 * sc_a : 0.f) + (in_b ? l_b0 * sc_b : 0.f);
-  const float inv = __builtin_amdgcn_rcpf(wave_sum_uniform(l_ab));
-  const float p_new = fast_exp2(lg_new - M) * inv;
-  const float out_scale = F8 ? inv * p.v_scale : inv;   // E4M3: values in code units until here
-  if (lane < ROWS) s_scw[wave][lane] = sc_a;
-  if (lane + kWave < ROWS) s_scw[wave][lane + kWave] = sc_b;
-
-  // Output: every wave takes CW columns; the SL lanes of one column (lanes c, c + CW, ...)
-  // each sum RS of the row groups, then fold their partial sums with lane swaps.
-  {
-    constexpr int SL = THREADS / D, CW = kWave / SL, RS = ROWS / SL;
-    static_assert(SL * CW == kWave && RS * SL == ROWS, "output split");
-    const int c = wave * CW + lane % CW, sl = lane / CW;
-    float v = 0.f;
-#pragma unroll
-    for (int j = 0; j < RS; ++j) {
-      const int r = sl * RS + j;
-      v = fmaf(s_red[r * D + c], s_scw[wave][r], v);
-    }
-#pragma unroll
-    for (int w = CW; w < kWave; w *= 2) v += __shfl_xor(v, w, kWave);
-    if (sl == 0) p.out[(size_t)unit * D + c] = v * out_scale;
-  }
-
-  uint64_t key = ~0ull;
-  float a = 0.f;
-  if (own) {
-    const float pj = fast_exp2(lg_own - M) * inv;
-    a = acc_old + pj;
-    acc[jo] = a;
-    if (full && pos_old <= limit)
-      key = score_key(policy_key(p.policy, p.policy_param, a, pj, pos_old), pos_old);
-  }
-  const uint64_t wmin = wave_min_u64_uniform(key);
-  if (lane == 0) s_key[wave] = wmin;
-  __syncthreads();                              // (2)
-  uint64_t best = s_key[0];
-#pragma unroll
-  for (int w = 1; w < S::WAVES; ++w) best = s_key[w] < best ? s_key[w] : best;
-
-  int dst = -1;
-  bool meta = false;
-  if (full) {
-    const uint64_t hit = __ballot(key == best && best != ~0ull);
-    const uint64_t grp = (hit >> ((lane / LANES) * LANES)) & ((1ull << LANES) - 1ull);
-    if (grp) dst = (__ffsll((unsigned long long)grp) - 1) * ROWS + g;
-    meta = key == best && best != ~0ull;
-  } else {
-    if (g == n % ROWS) dst = n;
-    meta = jo == n;
-  }
+  __syncthreads();                              // every K/V read is consumed
+  const Fold f = fold();
+  write_out(F8 ? f.inv * p.v_scale : f.inv);    // E4M3: values in code units until here
+  const int dst = choose(f);
   if (dst >= 0) {
     if constexpr (TP) {
       kst = s_new[0][rl];
@@ -440,13 +499,6 @@ void decode_resident_kernel(DecodeParams p) {
     }
     SC::store(ks + (size_t)dst * D + rl * VEC, kst);
     SC::store(vs + (size_t)dst * D + rl * VEC, vst);
-  }
-  if (meta) {                                   // the lane that wrote acc[dst] above, if any
-    pos[dst] = t;
-    acc[dst] = p_new;
-    if (p.victim_slot) p.victim_slot[unit] = full ? dst : -1;
-    if (p.evicted_pos) p.evicted_pos[unit] = full ? pos_old : -1;
-    if (p.evicted_acc) p.evicted_acc[unit] = full ? a : 0.f;
   }
 }
 
