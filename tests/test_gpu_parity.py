@@ -404,6 +404,38 @@ def test_stream_late_window_from_gpu_snapshot():
     torch.cuda.empty_cache()
 
 
+# More than 1024 units with 16-bit slots and k + 1 <= 7 row groups' worth take the
+# two-phase decode, whose 256-thread form decides (scores, argmin, bookkeeping) while the
+# V rows are in flight: filling from an empty cache (the append path), short prompts,
+# every policy, d = 64, k_local = 1 with all 112 slots used, and a ragged batch.
+TWO_PHASE = [
+    (Workload(900, "tp-fill-f16", 33, 1, 32, 128, "f16", 0, 150, 52, 52), None),
+    (Workload(901, "tp-short-bf16", 33, 1, 32, 128, "bf16", 40, 120, 52, 52), None),
+    (Workload(902, "tp-sinks-f16", 33, 1, 32, 128, "f16", 300, 60, 52, 52, policy="sinks",
+              policy_param=4, sinks=4), None),
+    (Workload(903, "tp-strided-bf16", 33, 1, 32, 128, "bf16", 300, 60, 52, 52,
+              policy="strided", policy_param=3), None),
+    (Workload(904, "tp-topk-f16", 33, 1, 32, 128, "f16", 300, 60, 52, 52, policy="topk"), None),
+    (Workload(905, "tp-d64-bf16", 65, 1, 16, 64, "bf16", 400, 80, 150, 60, heavy_frac=0.05), None),
+    (Workload(906, "tp-k1-f16", 33, 1, 32, 128, "f16", 200, 40, 110, 1), None),
+    (Workload(907, "tp-ragged-bf16", 40, 1, 32, 128, "bf16", 300, 60, 52, 52),
+     [300] + [int(v) for v in np.random.default_rng(5).integers(0, 301, size=39)]),
+]
+
+
+@pytest.mark.parametrize("w,lens", TWO_PHASE, ids=[w.name for w, _ in TWO_PHASE])
+def test_two_phase_decode_over_1024_units(w, lens):
+    from tests.parity import run_gpu_ragged
+    assert w.batch * w.heads > 1024
+    announce(f"[parity] {w.name}: units={w.batch * w.heads} k={w.k_heavy}+{w.k_local} "
+             f"T={w.prompt} n={w.steps} {w.policy} lens={'ragged' if lens else 'padded'}")
+    x = generate(w, seed=3, device="cuda")
+    r = run_gpu(w, x) if lens is None else run_gpu_ragged(w, x, lens)
+    agg = check_units(w, x, r, sample_units(w.units_per_layer, 24, seed=w.id), lens=lens)
+    announce(f"[parity] {w.name}: prefill {agg['prefill_out']:.2e} decode {agg['decode_out']:.2e} "
+             f"ties={len(agg['ties'])}")
+
+
 def test_fp32_long_prompts_with_sink_keys():
     # fp32 inputs, prompts of 1029 and up to 1218 keys with four sink keys each: over that
     # many keys, with a few dominating, an fp32 running sum of the prefill's softmax drifts
