@@ -78,7 +78,9 @@ __device__ __forceinline__ float row_sum(float v) {
 
 // Loads of one row group: K and V chunks of its U slots. Rows past the valid slots are
 // clamped to the new token's row (slots stored in T) or to slot 0 (E4M3 slots, whose rows
-// are replaced by the new token's codes once those are formed: fill_new_rows).
+// are replaced by the new token's codes once those are formed). E4M3: every K chunk is
+// issued before any V chunk, so that (the loads complete in order) the logits can be
+// formed while the V rows are still arriving.
 template <typename T, int D, int U, int THREADS, bool F8>
 __device__ __forceinline__ void load_rows(const typename SlotChunk<T, F8>::elem* ks,
                                           const typename SlotChunk<T, F8>::elem* vs,
@@ -91,9 +93,12 @@ __device__ __forceinline__ void load_rows(const typename SlotChunk<T, F8>::elem*
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = first + u * S::ROWS;
-      const size_t off = (size_t)(j < n ? j : 0) * D + rl * S::VEC;
-      kr[u] = SC::load(ks + off);
-      vr[u] = SC::load(vs + off);
+      kr[u] = SC::load(ks + (size_t)(j < n ? j : 0) * D + rl * S::VEC);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = first + u * S::ROWS;
+      vr[u] = SC::load(vs + (size_t)(j < n ? j : 0) * D + rl * S::VEC);
     }
   } else {
     // One base address per lane and a constant step per slot (row u is a valid slot when
@@ -175,11 +180,13 @@ __device__ __forceinline__ float chunk_dot(const uint4& a, const uint2& b, float
 
 // Logits (log2 domain) of a row group's U slots; slots past `last` are -inf.
 // Returns the group max, its sum of 2^(s - max) and the unnormalised out chunk.
-template <typename T, int D, int U, int THREADS, typename C>
+// FILLV (E4M3 slots): rows at and past `last` take the V codes `vnew` of the new token, so
+// that the V rows need not have landed before the logits are formed.
+template <typename T, int D, int U, int THREADS, typename C, bool FILLV = false>
 __device__ __forceinline__ void group_softmax(const uint4& qr, float qk_scale, const C (&kr)[U],
                                               const C (&vr)[U], int first, int last,
                                               float (&s)[U], float& mg, float& lg,
-                                              float (&o)[Shape<T, D>::VEC]) {
+                                              float (&o)[Shape<T, D>::VEC], const C& vnew = C{}) {
   using S = Shape<T, D, THREADS>;
   constexpr int VEC = S::VEC;
   mg = -INFINITY;
@@ -198,7 +205,8 @@ __device__ __forceinline__ void group_softmax(const uint4& qr, float qk_scale, c
     const float e = fast_exp2(s[u] - mref);
     lg += e;
     float vf[VEC];
-    unpack(vr[u], vf, T{});
+    if constexpr (FILLV) unpack(first + u * S::ROWS < last ? vr[u] : vnew, vf, T{});
+    else unpack(vr[u], vf, T{});
 #pragma unroll
     for (int i = 0; i < VEC; ++i) o[i] = fmaf(e, vf[i], o[i]);
   }
@@ -281,6 +289,11 @@ void decode_resident_kernel(DecodeParams p) {
   // g < n - u * ROWS (a compare against a uniform value), rows past the valid slots read
   // the new token's row.
   const size_t lane_off = (size_t)g * D + rl * VEC;
+  uint4 knr, vnr;
+  if constexpr (F8) {                           // first, so its codes are formed early
+    knr = ld16(kn + rl * VEC);
+    vnr = ld16(vn + rl * VEC);
+  }
   if constexpr (TP) {
     const SE* kb = ks + lane_off;
 #pragma unroll
@@ -294,8 +307,7 @@ void decode_resident_kernel(DecodeParams p) {
   const int jc = own ? jo : 0;
   const float acc_old = acc[jc];
   const int pos_old = pos[jc];
-  uint4 knr, vnr;
-  if constexpr (!TP) {
+  if constexpr (!TP && !F8) {
     knr = ld16(kn + rl * VEC);
     vnr = ld16(vn + rl * VEC);
   }
@@ -306,7 +318,9 @@ void decode_resident_kernel(DecodeParams p) {
   if constexpr (F8) {
     kst = quant_e4m3<T>(knr, p.k_inv);
     vst = quant_e4m3<T>(vnr, p.v_inv);
-    fill_new_rows<T, D, U, THREADS>(g, n, kst, vst, kr, vr);
+    // The new token's K codes join the rows now, its V codes at the PV product.
+#pragma unroll
+    for (int u = 0; u < U; ++u) kr[u] = g + u * ROWS < n ? kr[u] : kst;
   } else if constexpr (!TP) {
     kst = knr;
     vst = vnr;
@@ -475,7 +489,11 @@ void decode_resident_kernel(DecodeParams p) {
     }
     weigh_v();
   } else {
-    group_softmax<T, D, U, THREADS>(qr, p.qk_scale, kr, vr, g, n, s, mg, lg, o);
+    if constexpr (F8)
+      group_softmax<T, D, U, THREADS, typename SC::type, true>(qr, p.qk_scale, kr, vr, g, n, s, mg,
+                                                               lg, o, vst);
+    else
+      group_softmax<T, D, U, THREADS>(qr, p.qk_scale, kr, vr, g, n, s, mg, lg, o);
   }
 
 #pragma unroll
