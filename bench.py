@@ -57,9 +57,9 @@ METRIC = "H2O decode tokens/s at 20% KV budget + % of HBM roofline (prefill % MF
 DECODE_SOURCES = ("kv_cache_eviction_03_amd/csrc/decode.hip",
                   "kv_cache_eviction_03_amd/csrc/h2o_device.hpp")
 DECODE_TRAFFIC = {
-    "opt-6.7b-layer-fp16": {"sha256": "a411ffd43885a7b501dbd6a6bf21d06f20cbe9dba37370014b3610aa4d462476",
+    "opt-6.7b-layer-fp16": {"sha256": "a35bb581cf7bcdd20fbf300cb44b9fb7afe961bb168e44be80e2bfc2d0e04c1d",
                             "read_bytes": 14175279, "write_bytes": 376832},
-    "llama-7b-stack-bf16": {"sha256": "a411ffd43885a7b501dbd6a6bf21d06f20cbe9dba37370014b3610aa4d462476",
+    "llama-7b-stack-bf16": {"sha256": "a35bb581cf7bcdd20fbf300cb44b9fb7afe961bb168e44be80e2bfc2d0e04c1d",
                             "read_bytes": 113000816, "write_bytes": 3015295},
 }
 

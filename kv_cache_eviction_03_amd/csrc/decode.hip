@@ -28,7 +28,10 @@
 //     unnormalised out) in LDS; every wave folds them into scale factors with
 //     wave-uniform DPP reductions (the factors reach the output loop as scalars);
 //     owners update their scores and the (acc, pos) minimum is a wave fold plus
-//     an LDS stage. Two barriers, no global scratch.
+//     an LDS stage. Two barriers, no global scratch. Launches of many units take
+//     its two-phase form (TP below): K rows first, then V rows into the same
+//     registers, so that a lane holds half as many chunks and every workgroup of
+//     the launch is resident at once.
 //   * split: for larger k, two launches. split_partial gives S workgroups per
 //     unit one slot chunk each and writes (max, sum, unnormalised out) plus the
 //     chunk's logits to the workspace; split_combine (one 512-thread workgroup
@@ -50,8 +53,10 @@ constexpr int kBatch = 8;         // slot rows per row group in one load batch
 // step, and a deep model visits every other layer before it comes back to this one.
 constexpr bool kSlotNT = true;
 __device__ __forceinline__ uint4 ld_slot(const void* p) { return kSlotNT ? ld16_nt(p) : ld16(p); }
-// 256-thread launches with more units than this take the two-phase resident kernel: about
-// what the one-phase kernel (five workgroups per CU at 84 VGPRs) holds at once on 256 CUs.
+// 256-thread launches with more units than this take the two-phase resident kernel. The
+// one-phase kernel (76-90 VGPRs: five or six workgroups per CU, 1280-1536 on 256 CUs) runs
+// a launch it holds at once faster (OPT-6.7B layer, 256 units: 4.24 against 4.47 us), the
+// two-phase kernel one it does not (LLaMA-7B layer, 2048 units: 19.7 -> 19.4 us).
 constexpr int kTwoPhaseUnits = 1024;
 // The split partial kernel's: 7 makes 37 chunks of 112 slots for the 4096-slot stream
 // instead of 33 of 128 (the last holding one slot), 17.4 -> 17.1 us per step.
@@ -243,7 +248,7 @@ template <typename T, int D, int THREADS, bool F8, int UB = kBatch, bool TP = fa
 // OPT-30B layer's 411 need 7 of 8 at 1024 threads): one load and one logit fewer per lane.
 // Register budget: at most 128 VGPRs for the 256-thread shape, so that at least four
 // workgroups share a CU (three per CU measured 3.5% slower on the 32-layer LLaMA-7B-shaped
-// stack); fp16 / bf16 need about 92 with eight slots and 85 with seven (at 64 they spill);
+// stack); fp16 / bf16 need 84-90 with eight slots and 76-80 with seven (at 64 they spill);
 // the 1024-thread fp16 shape with seven ran the OPT-30B layer in 38.5 us against 38.9.
 // The E4M3 shapes with seven slots are held to 64 VGPRs (eight waves per SIMD) and fit
 // without spilling: the 256-thread one then runs eight workgroups per CU (the LLaMA-7B
